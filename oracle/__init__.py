@@ -1,0 +1,218 @@
+"""Oracle for the lightning-indexer hot path — TEST INFRASTRUCTURE ONLY.
+
+A plain fp64 CPU implementation (``idx_oracle.c``) of what the hot path computes:
+the MXFP4 / FP8 codecs, the K-cache store (RMSNorm -> NeoX RoPE -> quantise -> page
+store), the paged MQA logits with the causal/length mask, and the per-row top-k.
+Each C function cites the page passage it follows.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library and never imports it.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against
+closed forms, exhaustive or brute-force checks and invariants.  Parity unpinned: the
+absolute logits at realistic shapes rest only on those checks (the pages print no
+numeric example); the FP8 scale rule (amax / 448) is a reading, not a printed value.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "idx_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+FMT_MXFP4 = 0
+FMT_FP8 = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, no contraction, no fast-math, OpenMP)."""
+    os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+               "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            P, I64, I32, F32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_double
+            sig = {
+                "orc_e2m1_decode": (D, [ctypes.c_uint]),
+                "orc_e8m0_decode": (D, [ctypes.c_uint]),
+                "orc_e4m3_decode": (D, [ctypes.c_uint]),
+                "orc_e4m3_encode": (ctypes.c_uint8, [D]),
+                "orc_mxfp4_quant_block": (None, [P, P, P]),
+                "orc_bytes_per_token": (I64, [ctypes.c_int]),
+                "orc_k_store": (ctypes.c_int, [P, I64, I64, I64, I32, I32, P, I64, I64, P, F32, P, P, I32, P]),
+                "orc_k_rows_exact": (None, [P, I64, I64, P, F32, P, P, P]),
+                "orc_q_quant_mxfp4": (None, [P, I64, P, P]),
+                "orc_q_quant_fp8": (None, [P, P, I64, P, P]),
+                "orc_valid_len": (I64, [P, I32, I64]),
+                "orc_logits_paged": (ctypes.c_int, [P, I64, I64, I64, I32, I32, P, P, P, P, I32, P, I32, I32, I32,
+                                                    P, I64, P, I64]),
+                "orc_logits_exact": (None, [P, P, P, I64, P, I32, I32, I32, P, I64, P, I64]),
+                "orc_topk": (None, [P, I64, P, I32, I32, P, I64, P]),
+            }
+            for name, (res, args) in sig.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------------------- codecs
+def e2m1_decode(nibble: int) -> float:
+    return _load().orc_e2m1_decode(int(nibble))
+
+
+def e8m0_decode(byte: int) -> float:
+    return _load().orc_e8m0_decode(int(byte))
+
+
+def e4m3_decode(byte: int) -> float:
+    return _load().orc_e4m3_decode(int(byte))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().orc_e4m3_encode(float(v)))
+
+
+def mxfp4_quant_block(v) -> tuple[bytes, int]:
+    """Quantise 32 fp64 values: (16 packed nibble bytes, E8M0 scale byte)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    assert v.shape == (32,)
+    nib = np.zeros(16, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    _load().orc_mxfp4_quant_block(_p(v), _p(nib), _p(sc))
+    return nib.tobytes(), int(sc[0])
+
+
+def bytes_per_token(fmt: int) -> int:
+    return int(_load().orc_bytes_per_token(fmt))
+
+
+# ----------------------------------------------------------------------------- K store
+def k_store(pool: np.ndarray, offset: int, stride: int, num_pages: int, page_size: int, fmt: int,
+            k_bf16: np.ndarray, gamma: np.ndarray, eps: float, positions: np.ndarray, cos_sin: np.ndarray,
+            slots: np.ndarray) -> None:
+    """Write K rows into a host pool (uint8 array) in place."""
+    assert pool.dtype == np.uint8 and k_bf16.dtype == np.uint16 and k_bf16.shape[1] == 128
+    k_bf16 = np.ascontiguousarray(k_bf16)
+    gamma = np.ascontiguousarray(gamma, np.float32)
+    positions = np.ascontiguousarray(positions, np.int32)
+    cos_sin = np.ascontiguousarray(cos_sin, np.float32)
+    slots = np.ascontiguousarray(slots, np.int64)
+    rc = _load().orc_k_store(_p(pool), offset, stride, num_pages, page_size, fmt, _p(k_bf16), k_bf16.shape[0], 128,
+                             _p(gamma), float(eps), _p(positions), _p(cos_sin), cos_sin.shape[0], _p(slots))
+    if rc != 0:
+        raise ValueError("oracle k_store: invalid slot or position")
+
+
+def k_rows_exact(k_bf16, gamma, eps, positions, cos_sin) -> np.ndarray:
+    k_bf16 = np.ascontiguousarray(k_bf16, np.uint16)
+    out = np.empty((k_bf16.shape[0], 128), np.float64)
+    _load().orc_k_rows_exact(_p(k_bf16), k_bf16.shape[0], 128, _p(np.ascontiguousarray(gamma, np.float32)),
+                             float(eps), _p(np.ascontiguousarray(positions, np.int32)),
+                             _p(np.ascontiguousarray(cos_sin, np.float32)), _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------------- Q quant
+def q_quant_mxfp4(q_bf16: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """q_bf16 [..., 128] uint16 -> (packed [..., 64] uint8, scales [..., 4] uint8)."""
+    q = np.ascontiguousarray(q_bf16, np.uint16)
+    n = q.size // 128
+    qp = np.empty(q.shape[:-1] + (64,), np.uint8)
+    qs = np.empty(q.shape[:-1] + (4,), np.uint8)
+    _load().orc_q_quant_mxfp4(_p(q), n, _p(qp), _p(qs))
+    return qp, qs
+
+
+def q_quant_fp8(q_bf16: np.ndarray, w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """q_bf16 [..., H, 128], w [..., H] -> (e4m3 codes [..., H, 128], w with q scale folded)."""
+    q = np.ascontiguousarray(q_bf16, np.uint16)
+    w = np.ascontiguousarray(w, np.float32)
+    n = q.size // 128
+    assert w.size == n
+    q8 = np.empty(q.shape, np.uint8)
+    wo = np.empty(w.shape, np.float32)
+    _load().orc_q_quant_fp8(_p(q), _p(w), n, _p(q8), _p(wo))
+    return q8, wo
+
+
+# ----------------------------------------------------------------------------- scorer
+def valid_len(ctx: np.ndarray, n_q: int, r: int) -> int:
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    return int(_load().orc_valid_len(_p(ctx), n_q, r))
+
+
+def logits_paged(pool: np.ndarray, offset: int, stride: int, num_pages: int, page_size: int, fmt: int,
+                 q: np.ndarray, q_scale: np.ndarray | None, w: np.ndarray, page_table: np.ndarray,
+                 ctx: np.ndarray, B: int, n_q: int, H: int, out_stride: int,
+                 rows: np.ndarray | None = None) -> np.ndarray:
+    """fp64 logits [len(rows), out_stride]; cells s >= n_r are NaN."""
+    q = np.ascontiguousarray(q, np.uint8)
+    w = np.ascontiguousarray(w, np.float32)
+    pt = np.ascontiguousarray(page_table, np.int32)
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    if rows is None:
+        rows = np.arange(B * n_q, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, out_stride), np.float64)
+    qs = None if q_scale is None else np.ascontiguousarray(q_scale, np.uint8)
+    rc = _load().orc_logits_paged(_p(pool), offset, stride, num_pages, page_size, fmt, _p(q), _p(qs), _p(w), _p(pt),
+                                  pt.shape[1], _p(ctx), B, n_q, H, _p(rows), rows.size, _p(out), out_stride)
+    if rc != 0:
+        raise ValueError("oracle logits: page id outside the pool")
+    return out
+
+
+def logits_exact(q_rows: np.ndarray, w: np.ndarray, k_rows: np.ndarray, ctx: np.ndarray, n_q: int, H: int,
+                 out_stride: int, rows: np.ndarray) -> np.ndarray:
+    """Unquantised fp64 logits; q_rows [R, H, 128] fp64, k_rows [B, S, 128] fp64."""
+    q_rows = np.ascontiguousarray(q_rows, np.float64)
+    k_rows = np.ascontiguousarray(k_rows, np.float64)
+    w = np.ascontiguousarray(w, np.float32)
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, out_stride), np.float64)
+    _load().orc_logits_exact(_p(q_rows), _p(w), _p(k_rows), k_rows.shape[1] * 128, _p(ctx), k_rows.shape[0], n_q, H,
+                             _p(rows), rows.size, _p(out), out_stride)
+    return out
+
+
+# ----------------------------------------------------------------------------- top-k
+def topk(logits: np.ndarray, ctx: np.ndarray, n_q: int, k: int, rows: np.ndarray | None = None) -> np.ndarray:
+    """Indices [len(rows), k] in rank order (logit desc, index asc), -1 padded.
+
+    ``logits`` row i belongs to logical row rows[i] (fp32 inputs are widened exactly)."""
+    lg = np.ascontiguousarray(logits, np.float64)
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    if rows is None:
+        rows = np.arange(lg.shape[0], dtype=np.int64)
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, k), np.int32)
+    _load().orc_topk(_p(lg), lg.shape[1], _p(ctx), n_q, k, _p(rows), rows.size, _p(out))
+    return out

@@ -1,0 +1,161 @@
+"""Pins for the oracle's codecs (E2M1 / E8M0 / MXFP4 block rule / e4m3).
+
+Anchors: the literal format tables in tests/golden/formats.json (OCP MX and OFP8
+specifications, the formats the pages name), exact-rational re-derivations in
+tests/_indep.py, exhaustive tie and saturation cases, and power-of-two invariance.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import _indep as ind
+
+
+def test_e2m1_decode_matches_spec_table():
+    mags = ind.GOLDEN["e2m1_magnitudes"]["value"]
+    for code in range(16):
+        want = mags[code & 7] * (-1.0 if code & 8 else 1.0)
+        got = oracle.e2m1_decode(code)
+        assert got == want and np.signbit(got) == bool(code & 8), code
+
+
+def test_e8m0_decode():
+    assert oracle.e8m0_decode(127) == 1.0
+    assert oracle.e8m0_decode(0) == 2.0 ** -127
+    assert oracle.e8m0_decode(254) == 2.0 ** 127
+    assert np.isnan(oracle.e8m0_decode(255))
+    for b in range(255):
+        assert oracle.e8m0_decode(b) == 2.0 ** (b - 127)
+
+
+def test_e4m3_decode_matches_spec_points_and_structure():
+    for code, v in ind.GOLDEN["e4m3_points"]["value"]:
+        assert oracle.e4m3_decode(code) == v, code
+    for code in ind.GOLDEN["e4m3_nan_codes"]["value"]:
+        assert np.isnan(oracle.e4m3_decode(code))
+    finite = [oracle.e4m3_decode(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(finite, finite[1:])), "positive codes must be strictly increasing"
+    assert len(set(finite)) == 127 and max(finite) == 448.0
+    for c in range(0x7F):
+        assert Fraction(oracle.e4m3_decode(c)) == ind.E4M3_MAG[c]
+        assert oracle.e4m3_decode(c | 0x80) == -oracle.e4m3_decode(c)
+
+
+def _block_via_oracle(v):
+    nib, sc = oracle.mxfp4_quant_block(np.asarray(v, np.float64))
+    return ind.unpack_nibbles(nib), sc
+
+
+def test_mxfp4_worked_example_by_hand():
+    # amax = 6.5 -> floor(log2 6.5) = 2 -> X = 0 -> scale byte 127; then element by element:
+    # 6.5 -> saturates to 6 (code 7); -3 -> code 5 | sign; 1.25 is the midpoint of 1 and 1.5
+    # and goes to the even code 2 (value 1); 0.25 -> even code 0; -0.0 keeps its sign bit;
+    # 0.74 -> 0.5 (code 1); 0.75 -> midpoint of 0.5 and 1 -> even code 2; 5.0 -> midpoint of
+    # 4 and 6 -> even code 6 (value 4); 2.5 -> code 4 (value 2); 3.5 -> code 6 (value 4).
+    v = [6.5, -3.0, 1.25, 0.25, -0.0, 0.74, 0.75, 5.0, 2.5, 3.5] + [0.0] * 22
+    codes, sc = _block_via_oracle(v)
+    assert sc == 127
+    assert codes[:10] == [7, 13, 2, 0, 8, 1, 2, 6, 4, 6]
+    assert codes[10:] == [0] * 22
+
+
+def test_mxfp4_scale_rule_and_range():
+    rng = np.random.default_rng(1)
+    for _ in range(2000):
+        v = rng.standard_normal(32) * 2.0 ** rng.integers(-30, 30)
+        codes, sc = _block_via_oracle(v)
+        amax = np.abs(v).max()
+        ratio = amax / 2.0 ** (sc - 127)
+        assert 4.0 <= ratio < 8.0, (ratio, sc)
+
+
+def test_mxfp4_matches_exact_rational_quantiser():
+    rng = np.random.default_rng(2)
+    for t in range(3000):
+        kind = t % 3
+        if kind == 0:
+            v = rng.standard_normal(32)
+        elif kind == 1:  # values placed exactly on midpoints and grid points of a random scale
+            X = int(rng.integers(-10, 10))
+            grid = np.array([0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 7, 7.99])
+            v = rng.choice(grid, 32) * rng.choice([-1, 1], 32) * 2.0 ** X
+            v[0] = 7.0 * 2.0 ** X  # pins the scale
+        else:  # heavy tails and exact zeros
+            v = rng.standard_cauchy(32)
+            v[rng.integers(0, 32, 4)] = 0.0
+        codes, sc = _block_via_oracle(v)
+        want_codes, want_sc = ind.mxfp4_block_exact([Fraction(float(x)) for x in v],
+                                                    neg=[bool(np.signbit(x)) for x in v])
+        assert sc == want_sc
+        assert codes == want_codes, (v, codes, want_codes)
+
+
+def test_mxfp4_power_of_two_invariance():
+    rng = np.random.default_rng(3)
+    for _ in range(500):
+        v = rng.standard_normal(32)
+        base_codes, base_sc = _block_via_oracle(v)
+        for m in (-40, -7, -1, 1, 5, 60):
+            codes, sc = _block_via_oracle(v * 2.0 ** m)
+            assert codes == base_codes and sc == base_sc + m
+
+
+def test_mxfp4_saturation_and_zero_block():
+    codes, sc = _block_via_oracle([0.0] * 32)
+    assert sc == 0 and codes == [0] * 32
+    codes, sc = _block_via_oracle([-0.0] * 32)
+    assert sc == 0 and codes == [8] * 32
+    # every value in [6, 8) * 2^X (X fixed by amax = 7.9 * 2^X) saturates to code 7
+    X = 3
+    v = [7.9 * 2 ** X] + list(np.linspace(6.0, 7.99, 31) * 2 ** X)
+    codes, sc = _block_via_oracle(v)
+    assert sc == 127 + X and all(c == 7 for c in codes)
+
+
+def test_mxfp4_exponent_clamp():
+    codes, sc = _block_via_oracle([2.0 ** 200] + [0.0] * 31)
+    assert sc == 254  # X clamped to 127
+    codes, sc = _block_via_oracle([2.0 ** -300] + [0.0] * 31)
+    assert sc == 0 and codes[0] == 0  # X clamped to -127; the value is far below the grid
+
+
+def test_mxfp4_nibble_order():
+    v = np.zeros(32)
+    v[0], v[1] = 1.0 * 4, 6.0 * 4  # amax 24 -> X = 2 -> codes 2 (value 1) and 7 (value 6)
+    nib, sc = oracle.mxfp4_quant_block(v)
+    assert sc == 129 and nib[0] == (2 | (7 << 4))
+
+
+def test_e4m3_encode_exhaustive_points_midpoints_and_saturation():
+    mags = [oracle.e4m3_decode(c) for c in range(0x7F)]
+    for c, m in enumerate(mags):
+        assert oracle.e4m3_encode(m) == c
+        assert oracle.e4m3_encode(-m) == c | 0x80
+    for c in range(0x7E):
+        mid = (mags[c] + mags[c + 1]) / 2
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == want, c
+        assert oracle.e4m3_encode(np.nextafter(mid, 0)) == c
+        assert oracle.e4m3_encode(np.nextafter(mid, 1e9)) == c + 1
+    for big in (448.0, 449.0, 463.99, 464.0, 1e6, 1e300):
+        assert oracle.e4m3_encode(big) == 0x7E
+        assert oracle.e4m3_encode(-big) == 0xFE
+    assert oracle.e4m3_encode(-0.0) == 0x80
+    assert oracle.e4m3_encode(2.0 ** -11) == 0  # a quarter of the smallest subnormal
+
+
+def test_e4m3_encode_matches_exact_rational():
+    rng = np.random.default_rng(4)
+    vals = np.concatenate([rng.standard_normal(3000) * 100, rng.standard_normal(1000) * 0.01,
+                           rng.uniform(-460, 460, 1000)])
+    for x in vals:
+        assert oracle.e4m3_encode(float(x)) == ind.e4m3_code_exact(Fraction(float(x)), bool(np.signbit(x))), x
+
+
+def test_bytes_per_token_are_the_pages_numbers():
+    assert oracle.bytes_per_token(oracle.FMT_MXFP4) == ind.GOLDEN["mxfp4_bytes_per_token"]["value"]
+    assert oracle.bytes_per_token(oracle.FMT_FP8) == ind.GOLDEN["fp8_bytes_per_token"]["value"]
+    # 68 = 128 nibbles (64 B) + one E8M0 byte per 32-element block
+    assert 128 // 2 + 128 // ind.GOLDEN["mx_block_size"]["value"] == 68
