@@ -1,0 +1,214 @@
+/*
+ * idx.h — C ABI of the MI355X (gfx950) lightning-indexer hot path.
+ *
+ * The method (DeepSeek sparse attention's lightning indexer, as run on ROCm in the
+ * pages "[ROCm][Perf] Add AITER paged MXFP4 sparse indexing on gfx950" (vllm PR 57517)
+ * and "Dense MXFP4 indexer for DeepSeek-V4 on ROCm" (vllm PR 60834)) scores every
+ * cached token s against every query token t:
+ *
+ *     logits[t,s] = sum_h w[t,h] * ReLU( deq(q[t,h]) . deq(k[s]) )
+ *
+ * with one K row per cached token shared by all heads (MQA), K read in place from a
+ * paged cache through a page table (no gather pass), a causal / length mask, and a
+ * per-query top-k of the logits.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device memory must point to device memory of the current HIP
+ *    device; the caller owns all of it.  The library never allocates, frees or
+ *    synchronises, and keeps no state between calls apart from a per-device
+ *    architecture check done on first use.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *    stream) and returns before it finishes.  No entry point reads device memory on
+ *    the host, so every call can be captured in a HIP graph.
+ *  - Return value: IDX_OK, or a negative idx_status.  Argument problems are detected
+ *    on the host before anything is enqueued: IDX_EINVAL (null pointer, bad size or
+ *    range), IDX_EALIGN (misaligned pool offset / stride), IDX_EUNSUPPORTED (head dim
+ *    other than 128, page size not a multiple of 16 in [16, 1024], or no gfx950 device,
+ *    so the caller can fall back as the pages' FP8 default does).  IDX_EHIP reports a
+ *    HIP runtime error while enqueueing.
+ *  - Device data that breaks the stated contract (a page id outside the pool, a
+ *    context length above max_ctx) is never read out of bounds: such pages score
+ *    as NaN and lengths are clamped to max_ctx.
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_EINVAL = -1,
+  IDX_EUNSUPPORTED = -2,
+  IDX_EALIGN = -3,
+  IDX_EHIP = -4
+} idx_status;
+
+/* Indexer K-cache formats.
+ *  IDX_KV_MXFP4: 68 B per token — 128 E2M1 values (64 B) and four E8M0 block-32 scales
+ *                (page "Dense MXFP4 indexer for DeepSeek-V4 on ROCm", Purpose, gives the
+ *                MXFP4 indexer row as 68 B against FP8's 132 B).
+ *  IDX_KV_FP8_E4M3: 132 B per token — 128 OCP e4m3 codes and one fp32 per-token scale
+ *                (the default FP8 cache that passage compares with). */
+typedef enum { IDX_KV_MXFP4 = 0, IDX_KV_FP8_E4M3 = 1 } idx_kv_format;
+
+/* A zero-copy view of a caller-owned physical page pool.  Page "[ROCm][Perf] Add AITER
+ * paged MXFP4 sparse indexing on gfx950", Purpose, lists views of the cache taken without
+ * copies, explicit page strides into a shared pool, and page rebasing in 64 bits.
+ *
+ * Physical page `pid` starts at byte  base + offset_bytes + pid * page_stride_bytes,
+ * computed in 64 bits, so pools larger than 4 GiB work.  Inside a page of P tokens:
+ *   MXFP4: a nibble plane of P rows x 64 B (row r = token r; element 2j in the low
+ *          nibble of byte j, 2j+1 in the high nibble), then a scale plane of
+ *          P rows x 4 B (E8M0 byte of elements 32b..32b+31 at byte b).
+ *   FP8:   a code plane of P rows x 128 B (e4m3, element i at byte i), then P fp32
+ *          per-token scales.
+ * Bytes of a page beyond 68P (132P) and between pages are never touched. */
+typedef struct {
+  void* base;                /* device allocation holding the pool */
+  int64_t offset_bytes;      /* start of page 0 inside base; >= 0, multiple of 256 */
+  int64_t page_stride_bytes; /* distance between pages; >= page bytes, multiple of 256 */
+  int64_t num_pages;         /* physical pages addressable through the view; > 0 */
+  int32_t page_size;         /* tokens per page P: a multiple of 16 in [16, 1024] */
+  int32_t kv_format;         /* idx_kv_format */
+} idx_pool;
+
+/* ---------------------------------------------------------------------------------
+ * K-cache store (MXFP4): per row, RMSNorm over 128 dims, NeoX RoPE on the leading 64
+ * dims at the row's position, MXFP4 quantisation per 32-element block, and a store
+ * into the row's page slot.  Follows page "Dense MXFP4 indexer for DeepSeek-V4 on
+ * ROCm", Changes / K write (normalisation, rotation, MXFP4 packing and the page store
+ * happen in one pass with no intermediate written out) and page "[ROCm][Perf] Fuse DSA
+ * indexer QK preprocessing with AITER", Purpose (rotation covers the leading 64 dims;
+ * rows mapped to the padding slot are skipped).
+ *
+ * Arithmetic (all fp64; bit-exact against a CPU implementation of the same steps):
+ *   r = sqrt(S/128 + eps) with S summed as s_l = x_l^2 + x_{l+64}^2 (l < 64), then
+ *   halving s_l += s_{l+w} for w = 32..1;  y_i = (x_i / r) * gamma_i;
+ *   z_i = y_i c_i - y_{i+32} n_i,  z_{i+32} = y_{i+32} c_i + y_i n_i  (i < 32),
+ *   c_i = cos_sin[pos][i], n_i = cos_sin[pos][32+i];  z_i = y_i for i >= 64;
+ *   block scale X = clamp(floor(log2 amax) - 2, -127, 127), E8M0 byte X + 127
+ *   (byte 0 when amax = 0); element code = E2M1 round-to-nearest-even of z / 2^X,
+ *   saturating at 6, sign bit = IEEE sign of z.
+ *
+ * pool            IDX_KV_MXFP4 pool (see idx_pool).
+ * k_bf16          device, bf16 [n_rows][row_stride_elems] (first 128 elements used).
+ * n_rows          >= 0 (0 is a no-op); row_stride_elems >= 128.
+ * gamma           device, fp32 [128] RMSNorm weight; eps > 0 (fp32, widened to fp64).
+ * positions       device, int32 [n_rows], each in [0, max_pos).
+ * cos_sin         device, fp32 [max_pos][64]: 32 cosines then 32 sines per position.
+ * slot_mapping    device, int64 [n_rows]: page * P + row; negative = skip the row.
+ *                 Rows with a slot outside the pool, or a position outside
+ *                 [0, max_pos), are skipped as well.
+ * ------------------------------------------------------------------------------- */
+int idx_k_store_mxfp4(const idx_pool* pool, const void* k_bf16, int64_t n_rows, int64_t row_stride_elems,
+                      const float* gamma, float eps, const int32_t* positions, const float* cos_sin,
+                      int32_t max_pos, const int64_t* slot_mapping, void* stream);
+
+/* K-cache store (FP8 e4m3): the same normed, rotated row z, then one fp32 per-token
+ * scale sk = fp32(amax(|z|) / 448) and codes e4m3(z_i / sk), round-to-nearest-even,
+ * saturating at 448 (sk = 0 and sign-only zero codes for an all-zero row).  The FP8
+ * arm of the pages' MXFP4-versus-FP8 comparison (132 B per token).  Arguments as for
+ * idx_k_store_mxfp4, with an IDX_KV_FP8_E4M3 pool. */
+int idx_k_store_fp8(const idx_pool* pool, const void* k_bf16, int64_t n_rows, int64_t row_stride_elems,
+                    const float* gamma, float eps, const int32_t* positions, const float* cos_sin,
+                    int32_t max_pos, const int64_t* slot_mapping, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Q packing for the scorer (page "[ROCm][Perf] Add AITER paged MXFP4 sparse indexing on
+ * gfx950", Purpose: the integration produces packed MXFP4 Q with its scale layout).  Quantises n_vecs head vectors of 128
+ * bf16 values with the MXFP4 block rule above (no RoPE: the vectors are taken as
+ * already rotated).
+ * q_bf16   device, bf16 [n_vecs][128].
+ * q_packed device, uint8 [n_vecs][64] (element 2j in the low nibble of byte j).
+ * q_scale  device, uint8 [n_vecs][4] (E8M0 of blocks 0..3).
+ * ------------------------------------------------------------------------------- */
+int idx_q_quant_mxfp4(const void* q_bf16, int64_t n_vecs, uint8_t* q_packed, uint8_t* q_scale, void* stream);
+
+/* FP8 Q with one scale per 128-dim head vector, multiplied into that head's weight
+ * (page "[ROCm][Perf] Fuse DSA indexer QK preprocessing with AITER", Purpose: q is FP8
+ * quantised per token group and its scale is then folded into the indexer weights):
+ * sq = fp32(amax / 448), q_fp8[i] = e4m3(q[i] / sq), w_out = fp32(w * sq).
+ * q_bf16 device bf16 [n_vecs][128]; w device fp32 [n_vecs]; q_fp8 device uint8
+ * [n_vecs][128]; w_out device fp32 [n_vecs] (may alias w). */
+int idx_q_quant_fp8(const void* q_bf16, const float* w, int64_t n_vecs, uint8_t* q_fp8, float* w_out,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Paged MQA logits with the causal / length mask — the scorer.  Page "Dense MXFP4
+ * indexer for DeepSeek-V4 on ROCm", Purpose: the MQA-logits kernel reads the paged
+ * cache where it lies, so prefill needs no K gather; page "[ROCm][Perf] Add AITER paged
+ * MXFP4 sparse indexing on gfx950", Performance and accuracy: the isolated scorer
+ * timed at decode and prefill shapes.
+ *
+ * Rows: r = b * n_q + j is query token j of sequence b; its valid length is
+ *   n_r = clamp(ctx_lens[b] - n_q + 1 + j, 0, ctx_lens[b])
+ * (the n_q query tokens are the sequence's last n_q tokens, causal among
+ * themselves: decode n_q = 1, speculative verification n_q > 1, prefill n_q = ctx).
+ * For s < n_r:  logits[r * logits_stride + s] =
+ *   sum_h w[r*H + h] * max(0, sum_i deq(q[r,h])_i * deq(k_b[s])_i),
+ * k_b[s] read from physical page page_table[b * max_pages_per_seq + s / P], row s % P.
+ * Cells s >= n_r are not written.  Accumulation is fp32 (MFMA), results fp32.
+ *
+ * pool             MXFP4 or FP8 pool.
+ * q                device.  MXFP4: uint8 [B][n_q][H][64] packed E2M1;
+ *                  FP8: uint8 [B][n_q][H][128] e4m3.
+ * q_scale          device uint8 [B][n_q][H][4] E8M0 for MXFP4; ignored (may be NULL) for FP8.
+ * w                device fp32 [B][n_q][H] with every per-head factor already
+ *                  multiplied in (page "Dense MXFP4 indexer for DeepSeek-V4 on ROCm",
+ *                  Changes / Q quant: the Q op emits fp32 weights that carry the
+ *                  softmax and head scales).
+ * page_table       device int32 [B][max_pages_per_seq] physical page ids.
+ * ctx_lens         device int32 [B], each in [0, max_ctx].
+ * B, n_q >= 1; H in [1, 128]; D must be 128.
+ * max_ctx          host upper bound of ctx_lens (sizes the launch; no device read on
+ *                  the host); 0 <= max_ctx <= max_pages_per_seq * P and <= logits_stride.
+ * logits           device fp32 [B * n_q][logits_stride].
+ * ------------------------------------------------------------------------------- */
+int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                     const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
+                     int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Per-row top-k of the logits (page "Dense MXFP4 indexer for DeepSeek-V4 on ROCm",
+ * Purpose: the V4 indexer keeps the best 1024 tokens per query; page "[ROCm][Perf]
+ * Fuse DSA indexer QK preprocessing with AITER", Purpose: the selected indices land in
+ * a top-k index buffer).  For row r with valid length n_r (rule above):
+ *   n_r <= k: out_idx[r][0..n_r) = 0..n_r-1, the rest -1;
+ *   n_r >  k: the k token indices with the largest logits, equal logits broken
+ *             toward the smaller index (-0.0 equals +0.0), written in ascending index
+ *             order.
+ * Only cells s < n_r are read.  NaN logits are outside the contract.
+ * logits   device fp32 [B * n_q][logits_stride]; ctx_lens device int32 [B];
+ * max_ctx  host upper bound of ctx_lens, <= logits_stride; k >= 1;
+ * out_idx  device int32 [B * n_q][k].
+ * ------------------------------------------------------------------------------- */
+int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens, int32_t B, int32_t n_q,
+             int32_t max_ctx, int32_t k, int32_t* out_idx, void* stream);
+
+/* Diagnostic: quot[i] = a[i] / b[i] and root[i] = sqrt(a[i]) in fp64 on the device,
+ * with the same division and square-root operations the K store uses, so a test can
+ * confirm that they round exactly as IEEE-754 prescribes (the K store's bit-exactness
+ * rests on it).  Device fp64 arrays of n elements. */
+int idx_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n, void* stream);
+
+/* Bytes per token of a format (68, 132), or -1 for an unknown format. */
+int64_t idx_bytes_per_token(int32_t kv_format);
+
+/* IDX_OK when the current HIP device is gfx950, IDX_EUNSUPPORTED otherwise
+ * (including when no device is present). */
+int idx_device_check(void);
+
+/* Static description of a status code; never NULL. */
+const char* idx_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

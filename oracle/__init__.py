@@ -57,6 +57,7 @@ def _load():
                 "orc_e4m3_encode": (ctypes.c_uint8, [D]),
                 "orc_mxfp4_quant_block": (None, [P, P, P]),
                 "orc_bytes_per_token": (I64, [ctypes.c_int]),
+                "orc_num_threads": (ctypes.c_int, []),
                 "orc_k_store": (ctypes.c_int, [P, I64, I64, I64, I32, I32, P, I64, I64, P, F32, P, P, I32, P]),
                 "orc_k_rows_exact": (None, [P, I64, I64, P, F32, P, P, P]),
                 "orc_q_quant_mxfp4": (None, [P, I64, P, P]),
@@ -107,6 +108,11 @@ def mxfp4_quant_block(v) -> tuple[bytes, int]:
     sc = np.zeros(1, np.uint8)
     _load().orc_mxfp4_quant_block(_p(v), _p(nib), _p(sc))
     return nib.tobytes(), int(sc[0])
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 def bytes_per_token(fmt: int) -> int:

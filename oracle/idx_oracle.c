@@ -10,10 +10,11 @@
  *        (vllm PR 57517) — Purpose; Performance and accuracy (isolated scorer table);
  *        the statement that both MXFP4 kernels match the exact FP4-dequant reference.
  *   [p2] "Dense MXFP4 indexer for DeepSeek-V4 on ROCm" (vllm PR 60834) — Purpose
- *        (68 B per token instead of 132 B for FP8; MQA logits scored in place;
- *        cvt.rn.satfinite.e2m1x2 packing); Changes / K write (norm -> RoPE -> MXFP4 ->
- *        page store, nothing before the norm reaches memory); Changes / Q quant
- *        (fp32 weights with softmax and head scales folded in).
+ *        (an MXFP4 indexer row is 68 B against FP8's 132 B; the MQA-logits kernel
+ *        reads the cache in place; V4's packer uses cvt.rn.satfinite.e2m1x2);
+ *        Changes / K write (normalise, rotate, pack, store to the page in one pass);
+ *        Changes / Q quant (the fp32 weights arrive with softmax and head scales
+ *        multiplied in).
  *   [p3] "[ROCm][Perf] Fuse DSA indexer QK preprocessing with AITER" (vllm PR 53094)
  *        — Purpose (RoPE on the leading rope dims; per-token-group FP8 quantisation
  *        of q with the q scale folded into the weights; rows with a pad slot skipped).
@@ -27,6 +28,9 @@
  * floating-point operation below is one IEEE double operation, in the order written).
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -153,6 +157,15 @@ static double bf16_to_double(uint16_t h) {
 #define FMT_MXFP4 0
 #define FMT_FP8 1
 
+/* Threads the parallel loops below use (for reporting the CPU baseline honestly). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 int64_t orc_bytes_per_token(int fmt) { return fmt == FMT_MXFP4 ? 68 : (fmt == FMT_FP8 ? 132 : -1); }
 
 /* ------------------------------------------------------------------------------ */
@@ -211,11 +224,16 @@ int orc_k_store(uint8_t* pool, int64_t offset, int64_t stride, int64_t num_pages
                 const int32_t* positions, const float* cos_sin, int32_t max_pos, const int64_t* slots) {
   if (fmt != FMT_MXFP4 && fmt != FMT_FP8) return ORC_EINVAL;
   for (int64_t i = 0; i < n_rows; ++i) {
+    if (slots[i] >= 0 && (slots[i] / page_size >= num_pages || positions[i] < 0 || positions[i] >= max_pos))
+      return ORC_EINVAL;
+  }
+  /* rows are independent (each owns its slot), so they may run in any order */
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_rows; ++i) {
     int64_t slot = slots[i];
     if (slot < 0) continue;
     int64_t pid = slot / page_size, row = slot % page_size;
     int32_t pos = positions[i];
-    if (pid >= num_pages || pos < 0 || pos >= max_pos) return ORC_EINVAL;
     double z[HEAD_DIM];
     k_row_normed_roped(k_bf16 + i * row_stride, gamma, eps, cos_sin + (int64_t)pos * 64, z);
     uint8_t* page = pool + offset + pid * stride;

@@ -1,0 +1,145 @@
+"""ctypes binding of libidx.so (include/idx.h) — argument marshalling only.
+
+Each function carries the name of the C entry point it calls and takes torch tensors
+that already live on the current HIP device; it passes their data pointers, sizes and
+the current stream to the library and raises IdxError on a nonzero status.  No step of
+the hot path runs here: the work is done by the HIP kernels in the library.  If the
+library is missing the first call raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libidx.so")
+
+IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP = 0, -1, -2, -3, -4
+IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
+
+EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_q_quant_mxfp4", "idx_q_quant_fp8", "idx_logits_paged",
+           "idx_topk", "idx_diag_fp64", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
+
+
+class IdxError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class IdxPool(ctypes.Structure):
+    """Mirror of idx_pool."""
+    _fields_ = [("base", ctypes.c_void_p), ("offset_bytes", ctypes.c_int64), ("page_stride_bytes", ctypes.c_int64),
+                ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32), ("kv_format", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libidx.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"{p} not found: build it with `python -m sparse_attention_indexer_idx_amd.build`")
+    lib = ctypes.CDLL(p)
+    V, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    PP = ctypes.POINTER(IdxPool)
+    sigs = {
+        "idx_k_store_mxfp4": [PP, V, I64, I64, V, F32, V, V, I32, V, V],
+        "idx_k_store_fp8": [PP, V, I64, I64, V, F32, V, V, I32, V, V],
+        "idx_q_quant_mxfp4": [V, I64, V, V, V],
+        "idx_q_quant_fp8": [V, V, I64, V, V, V],
+        "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V],
+        "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
+        "idx_diag_fp64": [V, V, V, V, I64, V],
+        "idx_bytes_per_token": [I32],
+        "idx_device_check": [],
+        "idx_status_string": [ctypes.c_int],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.idx_bytes_per_token.restype = ctypes.c_int64
+    lib.idx_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().idx_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != IDX_OK:
+        raise IdxError(fn, status, status_string(status))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_pool(base, offset_bytes: int, page_stride_bytes: int, num_pages: int, page_size: int,
+              kv_format: int) -> IdxPool:
+    """An idx_pool view over the uint8 device tensor `base` (the caller keeps it alive)."""
+    return IdxPool(base.data_ptr(), offset_bytes, page_stride_bytes, num_pages, page_size, kv_format)
+
+
+def idx_k_store_mxfp4(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin, slot_mapping, stream=None):
+    _check("idx_k_store_mxfp4", load().idx_k_store_mxfp4(
+        ctypes.byref(pool), _ptr(k_bf16), k_bf16.shape[0], k_bf16.stride(0), _ptr(gamma), eps, _ptr(positions),
+        _ptr(cos_sin), cos_sin.shape[0], _ptr(slot_mapping), _stream(stream)))
+
+
+def idx_k_store_fp8(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin, slot_mapping, stream=None):
+    _check("idx_k_store_fp8", load().idx_k_store_fp8(
+        ctypes.byref(pool), _ptr(k_bf16), k_bf16.shape[0], k_bf16.stride(0), _ptr(gamma), eps, _ptr(positions),
+        _ptr(cos_sin), cos_sin.shape[0], _ptr(slot_mapping), _stream(stream)))
+
+
+def idx_q_quant_mxfp4(q_bf16, q_packed, q_scale, stream=None):
+    n = q_bf16.numel() // 128
+    _check("idx_q_quant_mxfp4", load().idx_q_quant_mxfp4(_ptr(q_bf16), n, _ptr(q_packed), _ptr(q_scale),
+                                                         _stream(stream)))
+
+
+def idx_q_quant_fp8(q_bf16, w, q_fp8, w_out, stream=None):
+    n = q_bf16.numel() // 128
+    _check("idx_q_quant_fp8", load().idx_q_quant_fp8(_ptr(q_bf16), _ptr(w), n, _ptr(q_fp8), _ptr(w_out),
+                                                     _stream(stream)))
+
+
+def idx_logits_paged(pool: IdxPool, q, q_scale, w, page_table, ctx_lens, B: int, n_q: int, H: int, max_ctx: int,
+                     logits, stream=None):
+    _check("idx_logits_paged", load().idx_logits_paged(
+        ctypes.byref(pool), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1], _ptr(ctx_lens),
+        B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), _stream(stream)))
+
+
+def idx_topk(logits, ctx_lens, B: int, n_q: int, max_ctx: int, k: int, out_idx, stream=None):
+    _check("idx_topk", load().idx_topk(_ptr(logits), logits.stride(0), _ptr(ctx_lens), B, n_q, max_ctx, k,
+                                       _ptr(out_idx), _stream(stream)))
+
+
+def idx_diag_fp64(a, b, quot, root, stream=None):
+    _check("idx_diag_fp64", load().idx_diag_fp64(_ptr(a), _ptr(b), _ptr(quot), _ptr(root), a.numel(),
+                                                 _stream(stream)))
+
+
+def idx_bytes_per_token(kv_format: int) -> int:
+    return int(load().idx_bytes_per_token(kv_format))
+
+
+def idx_device_check() -> int:
+    return int(load().idx_device_check())

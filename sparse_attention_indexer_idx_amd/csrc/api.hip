@@ -1,0 +1,209 @@
+// C-ABI entry points (include/idx.h): argument validation, the gfx950 gate, and the
+// hand-off to the kernel launchers.  Validation is plain host code that runs before
+// any HIP call, so every error path can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "idx.h"
+#include "launch.hpp"
+
+#define IDX_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_state[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return IDX_EUNSUPPORTED;
+  }
+  if (dev < kMaxDevices) {
+    const int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return IDX_OK;
+    if (st == 2) return IDX_EUNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return IDX_EUNSUPPORTED;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? IDX_OK : IDX_EUNSUPPORTED;
+}
+
+int64_t bytes_per_token(int32_t fmt) { return fmt == IDX_KV_MXFP4 ? 68 : (fmt == IDX_KV_FP8_E4M3 ? 132 : -1); }
+
+// Pool checks shared by every entry point that takes a pool.
+int check_pool(const idx_pool* p, int32_t want_fmt) {
+  if (!p || !p->base) return IDX_EINVAL;
+  if (p->kv_format != IDX_KV_MXFP4 && p->kv_format != IDX_KV_FP8_E4M3) return IDX_EINVAL;
+  if (want_fmt >= 0 && p->kv_format != want_fmt) return IDX_EINVAL;
+  if (p->page_size < 16 || p->page_size > 1024 || p->page_size % 16 != 0) return IDX_EUNSUPPORTED;
+  if (p->offset_bytes < 0 || p->num_pages <= 0 || p->page_stride_bytes <= 0) return IDX_EINVAL;
+  if (p->page_stride_bytes < bytes_per_token(p->kv_format) * p->page_size) return IDX_EINVAL;
+  if (p->offset_bytes % 256 != 0 || p->page_stride_bytes % 256 != 0) return IDX_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(p->base) & 255u) != 0) return IDX_EALIGN;
+  // the pool's byte span must fit in a signed 64-bit offset
+  if (p->num_pages > (INT64_MAX - p->offset_bytes) / p->page_stride_bytes) return IDX_EINVAL;
+  return IDX_OK;
+}
+
+idx::PoolView view_of(const idx_pool* p) {
+  idx::PoolView v;
+  v.base = static_cast<uint8_t*>(p->base) + p->offset_bytes;
+  v.stride = p->page_stride_bytes;
+  v.num_pages = p->num_pages;
+  v.page_size = p->page_size;
+  v.kv_format = p->kv_format;
+  return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_EHIP; }
+
+int k_store_common(const idx_pool* pool, int32_t fmt, const void* k_bf16, int64_t n_rows, int64_t row_stride_elems,
+                   const float* gamma, float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                   const int64_t* slot_mapping, void* stream) {
+  int st = check_pool(pool, fmt);
+  if (st != IDX_OK) return st;
+  if (n_rows < 0 || row_stride_elems < 128) return IDX_EINVAL;
+  if (n_rows > 0 && (!k_bf16 || !gamma || !positions || !cos_sin || !slot_mapping)) return IDX_EINVAL;
+  if (!(eps > 0.0f) || max_pos <= 0) return IDX_EINVAL;
+  if (n_rows > (int64_t)UINT32_MAX * 4) return IDX_EINVAL;
+  if ((st = check_device()) != IDX_OK) return st;
+  idx::KStoreArgs a;
+  a.pool = view_of(pool);
+  a.k = static_cast<const uint16_t*>(k_bf16);
+  a.n_rows = n_rows;
+  a.row_stride = row_stride_elems;
+  a.gamma = gamma;
+  a.eps = (double)eps;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.max_pos = max_pos;
+  a.slots = slot_mapping;
+  return hip_status(idx::launch_k_store(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+IDX_EXPORT int idx_k_store_mxfp4(const idx_pool* pool, const void* k_bf16, int64_t n_rows, int64_t row_stride_elems,
+                                 const float* gamma, float eps, const int32_t* positions, const float* cos_sin,
+                                 int32_t max_pos, const int64_t* slot_mapping, void* stream) {
+  return k_store_common(pool, IDX_KV_MXFP4, k_bf16, n_rows, row_stride_elems, gamma, eps, positions, cos_sin,
+                        max_pos, slot_mapping, stream);
+}
+
+IDX_EXPORT int idx_k_store_fp8(const idx_pool* pool, const void* k_bf16, int64_t n_rows, int64_t row_stride_elems,
+                               const float* gamma, float eps, const int32_t* positions, const float* cos_sin,
+                               int32_t max_pos, const int64_t* slot_mapping, void* stream) {
+  return k_store_common(pool, IDX_KV_FP8_E4M3, k_bf16, n_rows, row_stride_elems, gamma, eps, positions, cos_sin,
+                        max_pos, slot_mapping, stream);
+}
+
+IDX_EXPORT int idx_q_quant_mxfp4(const void* q_bf16, int64_t n_vecs, uint8_t* q_packed, uint8_t* q_scale,
+                                 void* stream) {
+  if (n_vecs < 0) return IDX_EINVAL;
+  if (n_vecs > 0 && (!q_bf16 || !q_packed || !q_scale)) return IDX_EINVAL;
+  if (n_vecs > (int64_t)UINT32_MAX * 64) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_packed) & 15u) != 0) return IDX_EALIGN;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  return hip_status(idx::launch_q_quant_mxfp4(static_cast<const uint16_t*>(q_bf16), n_vecs, q_packed, q_scale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int idx_q_quant_fp8(const void* q_bf16, const float* w, int64_t n_vecs, uint8_t* q_fp8, float* w_out,
+                               void* stream) {
+  if (n_vecs < 0) return IDX_EINVAL;
+  if (n_vecs > 0 && (!q_bf16 || !w || !q_fp8 || !w_out)) return IDX_EINVAL;
+  if (n_vecs > (int64_t)UINT32_MAX * 256) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_fp8) & 3u) != 0) return IDX_EALIGN;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  return hip_status(idx::launch_q_quant_fp8(static_cast<const uint16_t*>(q_bf16), w, n_vecs, q_fp8, w_out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                                const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
+                                int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
+                                int64_t logits_stride, void* stream) {
+  int st = check_pool(pool, -1);
+  if (st != IDX_OK) return st;
+  if (D != 128) return IDX_EUNSUPPORTED;
+  if (H < 1 || H > idx::kMaxHeads) return H < 1 ? IDX_EINVAL : IDX_EUNSUPPORTED;
+  if (B < 1 || n_q < 1 || max_ctx < 0 || max_pages_per_seq < 1 || logits_stride < 1) return IDX_EINVAL;
+  if (!q || !w || !page_table || !ctx_lens || !logits) return IDX_EINVAL;
+  if (pool->kv_format == IDX_KV_MXFP4 && !q_scale) return IDX_EINVAL;
+  if ((int64_t)max_ctx > (int64_t)max_pages_per_seq * pool->page_size) return IDX_EINVAL;
+  if ((int64_t)max_ctx > logits_stride) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q) & 15u) != 0) return IDX_EALIGN;
+  if ((int64_t)B * n_q > (int64_t)INT32_MAX) return IDX_EINVAL;
+  if ((st = check_device()) != IDX_OK) return st;
+  idx::LogitsArgs a;
+  a.pool = view_of(pool);
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.ctx = ctx_lens;
+  a.B = B;
+  a.n_q = n_q;
+  a.H = H;
+  a.max_ctx = max_ctx;
+  a.logits = logits;
+  a.lstride = logits_stride;
+  return hip_status(idx::launch_logits(a, static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens, int32_t B, int32_t n_q,
+                        int32_t max_ctx, int32_t k, int32_t* out_idx, void* stream) {
+  if (!logits || !ctx_lens || !out_idx) return IDX_EINVAL;
+  if (B < 1 || n_q < 1 || k < 1 || max_ctx < 0 || logits_stride < 1) return IDX_EINVAL;
+  if ((int64_t)max_ctx > logits_stride) return IDX_EINVAL;
+  if ((int64_t)B * n_q > (int64_t)INT32_MAX) return IDX_EINVAL;
+  if (max_ctx > idx::kTopkMaxCtx) return IDX_EUNSUPPORTED;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  idx::TopkArgs a;
+  a.logits = logits;
+  a.lstride = logits_stride;
+  a.ctx = ctx_lens;
+  a.B = B;
+  a.n_q = n_q;
+  a.max_ctx = max_ctx;
+  a.k = k;
+  a.out = out_idx;
+  return hip_status(idx::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int idx_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!a || !b || !quot || !root))) return IDX_EINVAL;
+  if (n > (int64_t)UINT32_MAX * 256) return IDX_EINVAL;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  return hip_status(idx::launch_diag_fp64(a, b, quot, root, n, static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int64_t idx_bytes_per_token(int32_t kv_format) { return bytes_per_token(kv_format); }
+
+IDX_EXPORT int idx_device_check(void) { return check_device(); }
+
+IDX_EXPORT const char* idx_status_string(int status) {
+  switch (status) {
+    case IDX_OK: return "ok";
+    case IDX_EINVAL: return "invalid argument";
+    case IDX_EUNSUPPORTED: return "unsupported shape, page size or device (needs gfx950, head dim 128)";
+    case IDX_EALIGN: return "misaligned pool offset, page stride or buffer";
+    case IDX_EHIP: return "HIP runtime error while enqueueing";
+    default: return "unknown status";
+  }
+}

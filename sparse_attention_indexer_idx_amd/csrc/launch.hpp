@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 kernels (defined next to each kernel) and the
+// argument bundles they take.  Arguments reaching these functions have already been
+// validated by the C-ABI layer (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+// A validated view of a physical page pool: page pid lives at
+// base + offset + pid * stride (64-bit arithmetic on the host and in the kernels).
+struct PoolView {
+  uint8_t* base;        // base + offset_bytes, pre-added
+  int64_t stride;       // bytes between pages
+  int64_t num_pages;
+  int32_t page_size;    // tokens per page
+  int32_t kv_format;    // 0 MXFP4, 1 FP8
+};
+
+struct KStoreArgs {
+  PoolView pool;
+  const uint16_t* k;
+  int64_t n_rows;
+  int64_t row_stride;
+  const float* gamma;
+  double eps;
+  const int32_t* positions;
+  const float* cos_sin;
+  int32_t max_pos;
+  const int64_t* slots;
+};
+
+struct LogitsArgs {
+  PoolView pool;
+  const uint8_t* q;
+  const uint8_t* q_scale;
+  const float* w;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* ctx;
+  int32_t B, n_q, H, max_ctx;
+  float* logits;
+  int64_t lstride;
+};
+
+struct TopkArgs {
+  const float* logits;
+  int64_t lstride;
+  const int32_t* ctx;
+  int32_t B, n_q, max_ctx, k;
+  int32_t* out;
+};
+
+hipError_t launch_k_store(const KStoreArgs& a, hipStream_t s);
+hipError_t launch_q_quant_mxfp4(const uint16_t* q, int64_t n_vecs, uint8_t* qp, uint8_t* qs, hipStream_t s);
+hipError_t launch_q_quant_fp8(const uint16_t* q, const float* w, int64_t n_vecs, uint8_t* q8, float* wo,
+                              hipStream_t s);
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n,
+                            hipStream_t s);
+
+// Largest context the top-k kernel supports (registers hold a row: 1024 threads x 64).
+constexpr int32_t kTopkMaxCtx = 65536;
+// Largest head count the scorer supports (8 head tiles of 16).
+constexpr int32_t kMaxHeads = 128;
+
+}  // namespace idx

@@ -30,7 +30,7 @@ GIB = 1 << 30
 
 MXFP4 = 0
 FP8 = 1
-BYTES_PER_TOKEN = {MXFP4: 68, FP8: 132}  # page 2, Purpose: 68 B per token instead of 132 B
+BYTES_PER_TOKEN = {MXFP4: 68, FP8: 132}  # "Dense MXFP4 indexer for DeepSeek-V4 on ROCm", Purpose
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -148,8 +148,10 @@ def _k_rows_for(ctx, page_table, page_size):
 
 
 def straddling_pages(page_stride: int, offset: int = 0):
-    """Page ids whose bytes span 2 GiB, 4 GiB, 4608 MiB and 4.608e9 B (the pages'
-    "2/4/4.608 GB address boundaries" read both as binary and decimal)."""
+    """Page ids whose bytes span 2 GiB, 4 GiB, 4608 MiB and 4.608e9 B: the address
+    boundaries at 2, 4 and 4.608 GB that the scorer's test coverage lists (page
+    "[ROCm][Perf] Add AITER paged MXFP4 sparse indexing on gfx950", Test plan), with
+    4.608 GB read both as binary and as decimal units."""
     out = []
     for boundary in (1 << 31, 1 << 32, 4608 << 20, 4_608_000_000):
         pid = (boundary - offset) // page_stride

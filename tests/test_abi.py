@@ -1,0 +1,147 @@
+"""The C ABI without a GPU: the library loads, exports every function include/idx.h
+declares, and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_indexer_idx_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idx.h")
+
+FAKE = 0x7F0000000000  # 256-aligned; never dereferenced (validation fails first, or no device)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*|size_t)\s+(idx_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from sparse_attention_indexer_idx_amd import build
+        build.build(verbose=False)
+    return bd.load()
+
+
+def no_gpu(lib):
+    return lib.idx_device_check() != bd.IDX_OK
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ("idx_k_store_mxfp4", "idx_logits_paged", "idx_topk", "idx_status_string"):
+        assert n in names
+    assert set(names) == set(bd.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(bd.status_string(st), str) and bd.status_string(st)
+
+
+def test_bytes_per_token(lib):
+    assert bd.idx_bytes_per_token(0) == 68 and bd.idx_bytes_per_token(1) == 132 and bd.idx_bytes_per_token(5) == -1
+
+
+def pool(**kw):
+    d = dict(base=FAKE, offset_bytes=0, page_stride_bytes=68 * 64, num_pages=16, page_size=64, kv_format=0)
+    d.update(kw)
+    return bd.IdxPool(d["base"], d["offset_bytes"], d["page_stride_bytes"], d["num_pages"], d["page_size"],
+                      d["kv_format"])
+
+
+def logits_call(lib, p=None, **kw):
+    a = dict(q=FAKE, qs=FAKE, w=FAKE, pt=FAKE, maxp=4, ctx=FAKE, B=2, n_q=1, H=4, D=128, max_ctx=256,
+             logits=FAKE, lstride=256)
+    a.update(kw)
+    p = p or pool()
+    return lib.idx_logits_paged(ctypes.byref(p), a["q"], a["qs"], a["w"], a["pt"], a["maxp"], a["ctx"], a["B"],
+                                a["n_q"], a["H"], a["D"], a["max_ctx"], a["logits"], a["lstride"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=64), bd.IDX_EUNSUPPORTED),
+    (dict(H=0), bd.IDX_EINVAL),
+    (dict(H=129), bd.IDX_EUNSUPPORTED),
+    (dict(B=0), bd.IDX_EINVAL),
+    (dict(n_q=0), bd.IDX_EINVAL),
+    (dict(q=None), bd.IDX_EINVAL),
+    (dict(qs=None), bd.IDX_EINVAL),          # MXFP4 needs scales
+    (dict(max_ctx=257), bd.IDX_EINVAL),      # > max_pages * P and > stride
+    (dict(lstride=100), bd.IDX_EINVAL),      # < max_ctx
+    (dict(max_ctx=-1), bd.IDX_EINVAL),
+    (dict(q=FAKE + 8), bd.IDX_EALIGN),
+])
+def test_logits_argument_checks(lib, kw, want):
+    assert logits_call(lib, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(page_size=48 + 1), bd.IDX_EUNSUPPORTED),
+    (dict(page_size=8), bd.IDX_EUNSUPPORTED),
+    (dict(page_size=2048, page_stride_bytes=68 * 2048), bd.IDX_EUNSUPPORTED),
+    (dict(page_stride_bytes=68 * 64 - 256), bd.IDX_EINVAL),     # smaller than a page
+    (dict(page_stride_bytes=68 * 64 + 16), bd.IDX_EALIGN),
+    (dict(offset_bytes=128), bd.IDX_EALIGN),
+    (dict(offset_bytes=-256), bd.IDX_EINVAL),
+    (dict(num_pages=0), bd.IDX_EINVAL),
+    (dict(kv_format=3), bd.IDX_EINVAL),
+    (dict(base=0), bd.IDX_EINVAL),
+    (dict(base=FAKE + 64), bd.IDX_EALIGN),
+    (dict(kv_format=1), bd.IDX_EINVAL),                          # FP8 page needs 132 B/token
+    (dict(num_pages=1 << 62, page_stride_bytes=1 << 20), bd.IDX_EINVAL),
+])
+def test_pool_checks(lib, kw, want):
+    assert logits_call(lib, p=pool(**kw)) == want
+
+
+def test_k_store_checks(lib):
+    P = pool()
+    args = lambda **kw: dict(dict(k=FAKE, n=10, rs=128, g=FAKE, eps=1e-6, pos=FAKE, cs=FAKE, mp=512, sl=FAKE), **kw)
+    def call(fn, p=P, **kw):
+        a = args(**kw)
+        return fn(ctypes.byref(p), a["k"], a["n"], a["rs"], a["g"], a["eps"], a["pos"], a["cs"], a["mp"], a["sl"], None)
+    assert call(lib.idx_k_store_mxfp4, rs=64) == bd.IDX_EINVAL
+    assert call(lib.idx_k_store_mxfp4, n=-1) == bd.IDX_EINVAL
+    assert call(lib.idx_k_store_mxfp4, eps=0.0) == bd.IDX_EINVAL
+    assert call(lib.idx_k_store_mxfp4, mp=0) == bd.IDX_EINVAL
+    assert call(lib.idx_k_store_mxfp4, sl=None) == bd.IDX_EINVAL
+    assert call(lib.idx_k_store_fp8) == bd.IDX_EINVAL            # an MXFP4 pool handed to the FP8 store
+    assert call(lib.idx_k_store_mxfp4, p=pool(kv_format=1, page_stride_bytes=132 * 64)) == bd.IDX_EINVAL
+
+
+def test_topk_checks(lib):
+    f = lib.idx_topk
+    assert f(None, 256, FAKE, 2, 1, 256, 64, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 256, FAKE, 2, 1, 257, 64, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 256, FAKE, 2, 1, 256, 0, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 1 << 20, FAKE, 2, 1, 65537, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
+
+
+def test_quant_checks(lib):
+    assert lib.idx_q_quant_mxfp4(FAKE, -1, FAKE, FAKE, None) == bd.IDX_EINVAL
+    assert lib.idx_q_quant_mxfp4(None, 4, FAKE, FAKE, None) == bd.IDX_EINVAL
+    assert lib.idx_q_quant_mxfp4(FAKE, 4, FAKE + 4, FAKE, None) == bd.IDX_EALIGN
+    assert lib.idx_q_quant_fp8(FAKE, None, 4, FAKE, FAKE, None) == bd.IDX_EINVAL
+
+
+def test_valid_calls_report_missing_device(lib):
+    """With arguments that pass validation, a machine without gfx950 gets EUNSUPPORTED
+    (the caller's signal to fall back), never a launch."""
+    if not no_gpu(lib):
+        pytest.skip("a GPU is present: fake pointers must not reach a launch")
+    assert logits_call(lib) == bd.IDX_EUNSUPPORTED
+    assert lib.idx_topk(FAKE, 256, FAKE, 2, 1, 256, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
+    assert lib.idx_q_quant_mxfp4(FAKE, 4, FAKE, FAKE, None) == bd.IDX_EUNSUPPORTED
+    # zero-sized work still goes through the device gate
+    assert lib.idx_device_check() == bd.IDX_EUNSUPPORTED

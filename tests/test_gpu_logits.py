@@ -1,0 +1,148 @@
+"""GPU parity: the paged MQA scorer against the oracle.
+
+K cache bytes and packed Q come from the oracle; the HIP scorer and the oracle read
+the same bytes.  Logits must meet max|d| <= 1e-4 * max|ref| and cosine >= 0.999999
+over the valid cells of each call; masked cells must keep the sentinel the buffer was
+filled with.  Full-size configurations are compared on sampled rows (all rows where
+the oracle finishes in seconds), always in the launch configuration of the full call."""
+import numpy as np
+import pytest
+
+from sparse_attention_indexer_idx_amd import binding as bd
+from sparse_attention_indexer_idx_amd import workloads as wl
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_scorer(W, fmt, rows_for_k=None):
+    """Device pool filled with the oracle's K bytes, oracle-packed Q, device tensors."""
+    hp = G.CompactHostPool(W, fmt, rows=rows_for_k)
+    pool = G.DevicePool(W, fmt)
+    pool.write_pages(hp.pids, hp.pages())
+    q, qs, w = G.oracle_q(W, fmt)
+    d = dict(pool=pool, hp=hp, q=q, qs=qs, w=w, q_d=G.dev(q), qs_d=None if qs is None else G.dev(qs), w_d=G.dev(w),
+             pt_d=G.dev(W.page_table), ctx_d=G.dev(W.ctx))
+    return d
+
+
+def run_scorer(W, d, stride=None):
+    torch = G.torch_cuda()
+    stride = stride or W.max_ctx
+    logits = torch.empty((W.rows, stride), dtype=torch.float32, device="cuda")
+    logits.view(torch.int32).fill_(np.int32(np.uint32(G.SENTINEL_BITS).view(np.int32)))
+    bd.idx_logits_paged(d["pool"].view, d["q_d"], d["qs_d"], d["w_d"], d["pt_d"], d["ctx_d"], W.B, W.n_q, W.H,
+                        W.max_ctx, logits)
+    torch.cuda.synchronize()
+    return logits
+
+
+def check(W, d, logits, rows, label):
+    got = logits.cpu().numpy()[rows]
+    ref = G.oracle_logits(d["hp"], d["q"], d["qs"], d["w"], rows, got.shape[1])
+    mask = G.valid_mask(W, rows, got.shape[1])
+    stats = G.assert_logits_close(got, ref, mask, label)
+    bits = got.view(np.uint32)
+    assert np.all(bits[~mask] == G.SENTINEL_BITS), f"{label}: a masked cell was written"
+    G.say(f"{label}: {stats}")
+    return got, ref, stats
+
+
+@pytest.mark.parametrize("cfg,fmt", [(0, wl.MXFP4), (0, wl.FP8), (1, wl.MXFP4), (3, wl.MXFP4), (3, wl.FP8)])
+def test_logits_all_rows(cfg, fmt):
+    W = wl.make_workload(cfg, kv_format=fmt)
+    G.say(f"logits cfg={cfg} fmt={fmt} rows={W.rows}")
+    d = setup_scorer(W, fmt)
+    logits = run_scorer(W, d)
+    check(W, d, logits, np.arange(W.rows), f"cfg{cfg}/fmt{fmt}")
+
+
+def test_logits_prefill_sampled_rows():
+    W = wl.make_workload(2)
+    G.say("logits prefill cfg=2 (8192 causal rows), sampled")
+    d = setup_scorer(W, wl.MXFP4)
+    logits = run_scorer(W, d)
+    rng = np.random.default_rng(50)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 17, 1023, 1024, 1025, 4095, 8190, 8191],
+                                     rng.integers(0, W.rows, 40)]))
+    check(W, d, logits, rows, "cfg2 sampled")
+
+
+@pytest.mark.parametrize("fmt", [wl.MXFP4, wl.FP8])
+def test_logits_large_pool_sampled_rows(fmt):
+    W = wl.make_workload(4, kv_format=fmt)
+    G.say(f"logits large pool fmt={fmt}, sampled")
+    # sequences holding the pages that straddle the address boundaries, plus random ones
+    strad = set(wl.straddling_pages(max(W.page_stride_bytes, W.page_bytes)))
+    seqs = [b for b in range(W.B) if strad & set(W.page_table[b].tolist())]
+    rng = np.random.default_rng(51)
+    seqs = np.unique(np.concatenate([seqs, rng.integers(0, W.B, 6), [0, W.B - 1]])).astype(np.int64)
+    d = setup_scorer(W, fmt)
+    logits = run_scorer(W, d)
+    check(W, d, logits, seqs, f"cfg4/fmt{fmt}")
+
+
+@pytest.mark.parametrize("H,n_q,P,ctx", [
+    (1, 1, 16, [1, 17, 300]),        # single head, tiny pages
+    (20, 2, 32, [0, 5, 100]),        # ragged head tile, empty sequence, n_q > ctx
+    (48, 1, 256, [700, 513]),        # 3 head tiles, large pages
+    (128, 1, 64, [129, 64]),         # the largest head count
+    (16, 9, 64, [200, 9, 3]),        # 9 head tiles -> the prefill kernel with several sequences
+    (32, 33, 128, [40, 1000]),       # prefill kernel, causal rows crossing chunk edges
+])
+def test_logits_shapes_and_edges(H, n_q, P, ctx):
+    rng = np.random.default_rng(H * 1000 + n_q)
+    ctx = np.array(ctx, np.int32)
+    B = ctx.size
+    need = [max((int(c) + P - 1) // P, 0) for c in ctx]
+    num_pages = max(sum(need), 1) + 5
+    perm = rng.permutation(num_pages)
+    pt = np.full((B, max(max(need), 1)), -1, np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        pt[b, :n] = perm[pos:pos + n]
+        pos += n
+    seq = np.repeat(np.arange(B, dtype=np.int32), ctx)
+    posn = np.concatenate([np.arange(int(c), dtype=np.int32) for c in ctx]) if ctx.sum() else np.zeros(0, np.int32)
+    slots = pt[seq, posn // P].astype(np.int64) * P + posn % P
+    W = wl.Workload(name="edge", B=B, n_q=n_q, H=H, page_size=P, topk=8, kv_format=wl.MXFP4, ctx=ctx,
+                    num_pages=num_pages, offset_bytes=512, page_stride_bytes=68 * P + 256, page_table=pt,
+                    k_rows=wl.f32_to_bf16_bits(rng.standard_normal((int(ctx.sum()), 128), dtype=np.float32)),
+                    k_seq=seq, positions=posn, slots=slots,
+                    q_rows=wl.f32_to_bf16_bits(rng.standard_normal((B, n_q, H, 128), dtype=np.float32)),
+                    w=(rng.standard_normal((B, n_q, H)) / np.sqrt(H)).astype(np.float32),
+                    gamma=np.ones(128, np.float32), eps=1e-6, cos_sin=wl.rope_cos_sin(max(int(ctx.max()), 1)),
+                    seed=0)
+    G.say(f"logits edge H={H} n_q={n_q} P={P} ctx={ctx.tolist()}")
+    d = setup_scorer(W, wl.MXFP4)
+    logits = run_scorer(W, d, stride=max(W.max_ctx, 1) + 3)
+    check(W, d, logits, np.arange(W.rows), f"edge H{H} nq{n_q} P{P}")
+
+
+def test_bad_page_id_scores_nan_without_faulting():
+    torch = G.torch_cuda()
+    W = wl.make_workload(0)
+    d = setup_scorer(W, wl.MXFP4)
+    pt = W.page_table.copy()
+    pt[1, 1] = W.num_pages + 1000     # outside the pool
+    pt[0, 0] = -7
+    d["pt_d"] = G.dev(pt)
+    logits = run_scorer(W, d)
+    got = logits.cpu().numpy()
+    P = W.page_size
+    bits = got.view(np.uint32)
+    for cells in (got[1, P: 2 * P], got[0, :P]):
+        assert np.all(np.isnan(cells))
+    # NaN was written (not the fill sentinel left untouched)
+    assert np.all(bits[1, P: 2 * P] != G.SENTINEL_BITS) and np.all(bits[0, :P] != G.SENTINEL_BITS)
+    good = np.isfinite(got[0, P:200])
+    assert good.all()
+    torch.cuda.synchronize()
+
+
+def test_scorer_deterministic():
+    W = wl.make_workload(3)
+    d = setup_scorer(W, wl.MXFP4)
+    a = run_scorer(W, d).cpu().numpy()
+    b = run_scorer(W, d).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
