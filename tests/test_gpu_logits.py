@@ -106,7 +106,7 @@ def test_logits_shapes_and_edges(H, n_q, P, ctx):
     posn = np.concatenate([np.arange(int(c), dtype=np.int32) for c in ctx]) if ctx.sum() else np.zeros(0, np.int32)
     slots = pt[seq, posn // P].astype(np.int64) * P + posn % P
     W = wl.Workload(name="edge", B=B, n_q=n_q, H=H, page_size=P, topk=8, kv_format=wl.MXFP4, ctx=ctx,
-                    num_pages=num_pages, offset_bytes=512, page_stride_bytes=68 * P + 256, page_table=pt,
+                    num_pages=num_pages, offset_bytes=512, page_stride_bytes=(68 * P + 256 + 255) // 256 * 256, page_table=pt,
                     k_rows=wl.f32_to_bf16_bits(rng.standard_normal((int(ctx.sum()), 128), dtype=np.float32)),
                     k_seq=seq, positions=posn, slots=slots,
                     q_rows=wl.f32_to_bf16_bits(rng.standard_normal((B, n_q, H, 128), dtype=np.float32)),
