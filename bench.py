@@ -45,7 +45,7 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(W, fmt, step_rows):
+def algorithmic_bytes(W, fmt, n_step_rows):
     """Bytes the method must move, per launch (valid cells only; masked cells,
     unused pool pages and the avoided K gather are excluded)."""
     bpt = 68 if fmt == 0 else 132
@@ -56,9 +56,25 @@ def algorithmic_bytes(W, fmt, step_rows):
     pages = int(sum((int(c) + W.page_size - 1) // W.page_size for c in W.ctx))
     scorer = tokens * bpt + q_b + W.rows * W.H * 4 + pages * 4 + W.B * 4 + n_valid * 4
     topk = n_valid * 4 + W.rows * W.topk * 4 + W.B * 4
-    kstore = step_rows * (256 + bpt + 4 + 8) + 128 * 4 + step_rows * 256
+    kstore = n_step_rows * (256 + bpt + 4 + 8) + 128 * 4 + n_step_rows * 256
     flops = n_valid * W.H * 2 * 128
     return {"scorer": scorer, "topk": topk, "kstore": kstore, "flops": flops, "valid_cells": n_valid}
+
+
+def decode_form(W):
+    """The scorer keeps every query row of a sequence in registers when
+    n_q * ceil(H/16) <= 16 (HBM-bound decode form); otherwise it runs its prefill form."""
+    return W.n_q * ((W.H + 15) // 16) <= 16
+
+
+def step_rows(W):
+    """K rows one step appends: the last n_q tokens of every sequence (all tokens for
+    a prefill chunk, one per sequence for plain decode)."""
+    rows = []
+    for o, c in zip(W.seq_row_offsets()[:-1], W.ctx):
+        n = min(W.n_q, int(c))
+        rows.append(np.arange(int(o) + int(c) - n, int(o) + int(c), dtype=np.int64))
+    return np.concatenate(rows)
 
 
 def source_hash(paths):
@@ -89,7 +105,6 @@ def cpu_baseline(W, fmt, budget_s):
     rows, logits of every row, top-k of every row) for the decode workloads; for the
     prefill workload a bounded sample of rows, scaled to one step."""
     import oracle
-    step_rows = W.B if W.n_q == 1 else W.k_rows.shape[0]
     pt = W.page_table
     pids = np.unique(pt[pt >= 0]).astype(np.int64)
     remap = np.full(W.num_pages, -1, np.int64)
@@ -112,8 +127,7 @@ def cpu_baseline(W, fmt, budget_s):
     else:
         rng = np.random.default_rng(7)
         sample_rows = np.sort(rng.choice(W.rows, 256, replace=False)).astype(np.int64)
-    new = np.arange(W.k_rows.shape[0]) if step_rows == W.k_rows.shape[0] else \
-        np.concatenate([[int(o) + int(c) - 1] for o, c in zip(W.seq_row_offsets()[:-1], W.ctx)])
+    new = step_rows(W)
     times = []
     t_end = time.perf_counter() + budget_s
     while True:
@@ -156,7 +170,7 @@ def main():
     used_bytes = int(np.minimum(W.ctx, W.max_ctx).sum()) * (68 if fmt == 0 else 132)
     # Prefill re-reads its small K from L2 by design and writes far more logits than
     # the last-level cache holds, so only decode rotates pool replicas.
-    prefill_like = W.n_q * ((W.H + 15) // 16) > 8
+    prefill_like = not decode_form(W)
     replicas = 1 if (args.warm or prefill_like) else max(2, int(np.ceil(2 * LLC_BYTES / max(used_bytes, 1))) + 1)
     replicas = min(replicas, 16, max(1, int((64 << 30) // pool_bytes)))
 
@@ -187,10 +201,7 @@ def main():
     pt, ctx = dev(W.page_table), dev(W.ctx)
     logits = torch.empty((W.rows, W.max_ctx), dtype=torch.float32, device="cuda")
     out = torch.empty((W.rows, W.topk), dtype=torch.int32, device="cuda")
-    if W.n_q == 1:  # decode: the step stores each sequence's newest token
-        new = np.array([int(o) + int(c) - 1 for o, c in zip(W.seq_row_offsets()[:-1], W.ctx)], np.int64)
-    else:           # prefill: the step stores every token of the chunk
-        new = np.arange(W.k_rows.shape[0], dtype=np.int64)
+    new = step_rows(W)
     k_new, pos_new, slot_new = k_all[dev(new)], positions[dev(new)], slots[dev(new)]
     torch.cuda.synchronize()
 
@@ -228,7 +239,7 @@ def main():
     src = [os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in
            ("logits.hip", "device_common.hpp", "launch.hpp")]
     shash = source_hash(src)
-    prefill = W.n_q * ((W.H + 15) // 16) > 8
+    prefill = not decode_form(W)
     if prefill:
         achieved = ab["flops"] / (s_us.mean() * 1e-6) / 1e12
         peak = FP4_PEAK_TFLOPS if fmt == 0 else FP8_PEAK_TFLOPS

@@ -23,7 +23,7 @@
  *  - Return value: IDX_OK, or a negative idx_status.  Argument problems are detected
  *    on the host before anything is enqueued: IDX_EINVAL (null pointer, bad size or
  *    range), IDX_EALIGN (misaligned pool offset / stride), IDX_EUNSUPPORTED (head dim
- *    other than 128, page size not a multiple of 16 in [16, 1024], or no gfx950 device,
+ *    other than 128, page size not a power of two in [16, 1024], or no gfx950 device,
  *    so the caller can fall back as the pages' FP8 default does).  IDX_EHIP reports a
  *    HIP runtime error while enqueueing.
  *  - Device data that breaks the stated contract (a page id outside the pool, a
@@ -73,7 +73,7 @@ typedef struct {
   int64_t offset_bytes;      /* start of page 0 inside base; >= 0, multiple of 256 */
   int64_t page_stride_bytes; /* distance between pages; >= page bytes, multiple of 256 */
   int64_t num_pages;         /* physical pages addressable through the view; > 0 */
-  int32_t page_size;         /* tokens per page P: a multiple of 16 in [16, 1024] */
+  int32_t page_size;         /* tokens per page P: a power of two in [16, 1024] */
   int32_t kv_format;         /* idx_kv_format */
 } idx_pool;
 
@@ -167,6 +167,8 @@ int idx_q_quant_fp8(const void* q_bf16, const float* w, int64_t n_vecs, uint8_t*
  * B, n_q >= 1; H in [1, 128]; D must be 128.
  * max_ctx          host upper bound of ctx_lens (sizes the launch; no device read on
  *                  the host); 0 <= max_ctx <= max_pages_per_seq * P and <= logits_stride.
+ *                  When n_q * ceil(H/16) > 16 (the prefill form) max_ctx is limited to
+ *                  16384 * P (IDX_EUNSUPPORTED beyond).
  * logits           device fp32 [B * n_q][logits_stride].
  * ------------------------------------------------------------------------------- */
 int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,

@@ -28,6 +28,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     # Packed fp32 VALU forms are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the epilogue reads them directly (no v_accvgpr_read per element).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -45,7 +45,7 @@ int check_pool(const idx_pool* p, int32_t want_fmt) {
   if (!p || !p->base) return IDX_EINVAL;
   if (p->kv_format != IDX_KV_MXFP4 && p->kv_format != IDX_KV_FP8_E4M3) return IDX_EINVAL;
   if (want_fmt >= 0 && p->kv_format != want_fmt) return IDX_EINVAL;
-  if (p->page_size < 16 || p->page_size > 1024 || p->page_size % 16 != 0) return IDX_EUNSUPPORTED;
+  if (p->page_size < 16 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)) != 0) return IDX_EUNSUPPORTED;
   if (p->offset_bytes < 0 || p->num_pages <= 0 || p->page_stride_bytes <= 0) return IDX_EINVAL;
   if (p->page_stride_bytes < bytes_per_token(p->kv_format) * p->page_size) return IDX_EINVAL;
   if (p->offset_bytes % 256 != 0 || p->page_stride_bytes % 256 != 0) return IDX_EALIGN;
@@ -61,6 +61,7 @@ idx::PoolView view_of(const idx_pool* p) {
   v.stride = p->page_stride_bytes;
   v.num_pages = p->num_pages;
   v.page_size = p->page_size;
+  v.page_shift = __builtin_ctz((unsigned)p->page_size);
   v.kv_format = p->kv_format;
   return v;
 }
@@ -146,6 +147,7 @@ IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const ui
   if ((int64_t)max_ctx > logits_stride) return IDX_EINVAL;
   if ((reinterpret_cast<uintptr_t>(q) & 15u) != 0) return IDX_EALIGN;
   if ((int64_t)B * n_q > (int64_t)INT32_MAX) return IDX_EINVAL;
+  if ((int64_t)max_ctx > idx::logits_max_ctx(n_q, H, pool->page_size)) return IDX_EUNSUPPORTED;
   if ((st = check_device()) != IDX_OK) return st;
   idx::LogitsArgs a;
   a.pool = view_of(pool);

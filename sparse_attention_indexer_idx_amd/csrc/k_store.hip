@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
   }
   const double z1 = y1;
 
-  const int64_t pid = slot / P, prow = slot % P;
+  const int64_t pid = slot >> a.pool.page_shift, prow = slot & (P - 1);
   uint8_t* page = a.pool.base + pid * a.pool.stride;
 
   if (FMT == 0) {

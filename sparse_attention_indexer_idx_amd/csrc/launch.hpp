@@ -14,7 +14,8 @@ struct PoolView {
   uint8_t* base;        // base + offset_bytes, pre-added
   int64_t stride;       // bytes between pages
   int64_t num_pages;
-  int32_t page_size;    // tokens per page
+  int32_t page_size;    // tokens per page (a power of two)
+  int32_t page_shift;   // log2(page_size)
   int32_t kv_format;    // 0 MXFP4, 1 FP8
 };
 
@@ -57,6 +58,11 @@ hipError_t launch_q_quant_mxfp4(const uint16_t* q, int64_t n_vecs, uint8_t* qp, 
 hipError_t launch_q_quant_fp8(const uint16_t* q, const float* w, int64_t n_vecs, uint8_t* q8, float* wo,
                               hipStream_t s);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
+// Whether the scorer takes its decode form (all query rows of a sequence in registers).
+bool logits_uses_decode_kernel(int n_q, int H);
+// Largest max_ctx the scorer accepts for this shape (the prefill form splits the context
+// into at most 256 chunks of at most 64 pages).
+int64_t logits_max_ctx(int n_q, int H, int page_size);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n,
                             hipStream_t s);

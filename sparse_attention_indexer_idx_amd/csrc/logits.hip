@@ -15,6 +15,12 @@
 // per lane and finishes the head sum with a 4x16 transpose-reduce (three lane swaps).
 // FP8 uses the same instruction with e4m3 operands, unit block scales, and the fp32
 // per-token K scale applied to the weighted partial sums.
+//
+// Page ids are looked up once per wave (decode) or once per 64 pages (prefill, one id
+// per lane, read back with readlane), always before the K loads they address, so the
+// only dependent memory round trip is page id -> K bytes.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -23,44 +29,35 @@ namespace {
 
 constexpr int kHeadTile = 16;
 
-struct Page {
-  const uint8_t* base;  // start of the physical page, or null for an invalid page id
-};
-
-__device__ __forceinline__ Page page_of(const LogitsArgs& a, int b, int64_t s) {
-  const int32_t pid = a.page_table[(int64_t)b * a.max_pages + s / a.pool.page_size];
-  Page p;
-  p.base = (pid >= 0 && pid < a.pool.num_pages) ? a.pool.base + (int64_t)pid * a.pool.stride : nullptr;
-  return p;
-}
-
 // Valid length of query j of a sequence with n_b cached tokens.
 __device__ __forceinline__ int valid_len(int n_b, int n_q, int j) {
   int n = n_b - n_q + 1 + j;
   return n < 0 ? 0 : (n > n_b ? n_b : n);
 }
 
-// B operand (16 tokens starting at page row `row0`) and the lane's scale byte / fp32
-// token scale.  FMT 0: 16 B nibbles + E8M0 byte; FMT 1: 32 B e4m3 + fp32 scale.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// B operand (16 tokens starting at page row `row0` of `page`) and the lane's scale.
+// FMT 0: 16 B nibbles + E8M0 byte; FMT 1: 32 B e4m3 + fp32 token scale bits.
 template <int FMT>
 struct KTile {
   v8i v;
-  uint32_t scale;  // E8M0 byte in bits 0..7 (MXFP4) or fp32 bits of the token scale (FP8)
+  uint32_t scale;
 };
 
 template <int FMT>
-__device__ __forceinline__ KTile<FMT> load_k_tile(const uint8_t* page, int P, int row0, int lane) {
+__device__ __forceinline__ KTile<FMT> load_k_tile(const uint8_t* __restrict__ page, int P, int row0, int lane) {
   KTile<FMT> t;
-  const int tok = row0 + (lane & 15), g = lane >> 4;
+  const uint32_t tok = (uint32_t)(row0 + (lane & 15)), g = (uint32_t)(lane >> 4);
   if (FMT == 0) {
-    const uint4 x = *(const uint4*)(page + (int64_t)tok * 64 + 16 * g);
+    const uint4 x = *(const uint4*)(page + (tok * 64u + 16u * g));
     t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-    t.scale = page[(int64_t)P * 64 + tok * 4 + g];
+    t.scale = page[(uint32_t)P * 64u + tok * 4u + g];
   } else {
-    const uint4* src = (const uint4*)(page + (int64_t)tok * 128 + 32 * g);
+    const uint4* src = (const uint4*)(page + (tok * 128u + 32u * g));
     const uint4 x = src[0], y = src[1];
     t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-    t.scale = *(const uint32_t*)(page + (int64_t)P * 128 + tok * 4);
+    t.scale = *(const uint32_t*)(page + ((uint32_t)P * 128u + tok * 4u));
   }
   return t;
 }
@@ -107,49 +104,71 @@ __device__ __forceinline__ v4f mfma(const v8i& A, uint32_t sa, const KTile<FMT>&
                                                            (int)kE8m0One);
 }
 
+// ReLU on the fp32 bit pattern: every negative value (and -0.0) has a negative int32
+// pattern, so an integer max with 0 is ReLU in one instruction, with none of the NaN
+// canonicalisation a floating-point max carries.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// acc + sum_i w_i * ReLU(d_i) as one multiply-add chain (first: start from w_0 * ReLU(d_0)).
+__device__ __forceinline__ float relu_dot_acc(const v4f& d, const v4f& w, float acc, bool first) {
+  float s = first ? w[0] * relu(d[0]) : fmaf(w[0], relu(d[0]), acc);
+  s = fmaf(w[1], relu(d[1]), s);
+  s = fmaf(w[2], relu(d[2]), s);
+  s = fmaf(w[3], relu(d[3]), s);
+  return s;
+}
+
 __device__ __forceinline__ float relu_dot(const v4f& d, const v4f& w) {
-  float s = w[0] * fmaxf(d[0], 0.0f);
-  s += w[1] * fmaxf(d[1], 0.0f);
-  s += w[2] * fmaxf(d[2], 0.0f);
-  s += w[3] * fmaxf(d[3], 0.0f);
+  float s = w[0] * relu(d[0]);
+  s += w[1] * relu(d[1]);
+  s += w[2] * relu(d[2]);
+  s += w[3] * relu(d[3]);
   return s;
 }
 
 // ------------------------------------------------------------------------------------
-// Decode: every query row of a sequence in registers (n_q * ceil(H/16) <= 8 head tiles),
-// one wave per 64 consecutive cached tokens (four 16-token tiles), 4 waves per block.
-// grid = (ceil(max_ctx / 256), B).
+// Decode: every query row of a sequence in registers (n_q * ceil(H/16) <= 16 head
+// tiles), one wave per 64 consecutive cached tokens (four 16-token tiles), 4 waves per
+// block; grid = (ceil(max_ctx / 256), B).  Per wave: the page ids of its four tiles and
+// the sequence length are fetched together, then all K, Q and weight loads are issued
+// before the first use.
 // ------------------------------------------------------------------------------------
-constexpr int kDecodeMaxTiles = 8;
+constexpr int kDecodeMaxTiles = 16;
 constexpr int kDecodeTokPerWave = 64;
 constexpr int kDecodeWaves = 4;
 
 template <int FMT, int NT>
 __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
   const int b = blockIdx.y;
-  const int n_b = min(max(a.ctx[b], 0), a.max_ctx);
   const int tok0 = (blockIdx.x * kDecodeWaves + wave) * kDecodeTokPerWave;
-  if (tok0 >= n_b) return;
-  const int HT = (a.H + kHeadTile - 1) / kHeadTile;
-  const int P = a.pool.page_size;
+  if (tok0 >= a.max_ctx) return;
+  const int P = a.pool.page_size, lgP = a.pool.page_shift;
+  const int last_page = (a.max_ctx - 1) >> lgP;
+  const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
 
-  // Issue the K loads of all four tiles first (the whole 64-token span in flight).
+  int32_t pid[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pid[t] = uniform(ptb[std::min((tok0 + 16 * t) >> lgP, last_page)]);
+  const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
+  if (tok0 >= n_b) return;
+
+  // K tiles: a tile past the sequence end or on an invalid page reads page 0 row 0
+  // (always inside the pool) and is masked below.
   KTile<FMT> kt[4];
   bool ok[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int s0 = tok0 + 16 * t;
-    ok[t] = false;
-    if (s0 < n_b) {
-      const Page pg = page_of(a, b, s0);
-      if (pg.base) {
-        kt[t] = load_k_tile<FMT>(pg.base, P, s0 % P, lane);
-        ok[t] = true;
-      }
-    }
+    const bool valid_page = pid[t] >= 0 && (int64_t)pid[t] < a.pool.num_pages;
+    const int64_t p = valid_page ? pid[t] : 0;
+    const uint8_t* page = a.pool.base + p * a.pool.stride;
+    kt[t] = load_k_tile<FMT>(page, P, valid_page ? (s0 & (P - 1)) : 0, lane);
+    ok[t] = valid_page;  // tiles past n_b are computed but never stored
   }
 
+  const int HT = (a.H + kHeadTile - 1) / kHeadTile;
   v8i qa[NT];
   uint32_t qs[NT];
   v4f qw[NT];
@@ -162,23 +181,24 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
   }
 
   const float qnan = __builtin_nanf("");
+  const int s = tok0 + lane;
   for (int j = 0; j < a.n_q; ++j) {
     float p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float acc = 0.0f;
-      if (ok[t]) {
+      bool first = true;
 #pragma unroll
-        for (int m = 0; m < NT; ++m)
-          if (m / HT == j) acc += relu_dot(mfma<FMT>(qa[m], qs[m], kt[t]), qw[m]);
-        if (FMT == 1) acc *= __uint_as_float(kt[t].scale);
-      } else {
-        acc = qnan;
-      }
-      p[t] = acc;
+      for (int m = 0; m < NT; ++m)
+        if (m / HT == j) {
+          const float v = relu_dot(mfma<FMT>(qa[m], qs[m], kt[t]), qw[m]);
+          acc = first ? v : acc + v;
+          first = false;
+        }
+      if (FMT == 1) acc *= __uint_as_float(kt[t].scale);
+      p[t] = ok[t] ? acc : qnan;
     }
     const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
-    const int s = tok0 + lane;
     if (s < valid_len(n_b, a.n_q, j)) a.logits[((int64_t)b * a.n_q + j) * a.lstride + s] = logit;
   }
 }
@@ -187,11 +207,13 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
 // Prefill / long query sets: each wave owns 4 query rows (one per lane group after the
 // transpose-reduce) and walks 16-token K tiles; a block is 4 waves = 16 rows.  Work
 // units are (16-row block, token chunk) pairs enumerated chunk-major from a host-built
-// table so that no unit is empty and all units have similar cost.
+// table so that no unit is empty and all units have similar cost.  The wave keeps the
+// physical ids of the next 64 logical pages one per lane.
 // ------------------------------------------------------------------------------------
 constexpr int kPrefillRowsPerWave = 4;
 constexpr int kPrefillRowsPerBlock = 16;
 constexpr int kMaxChunks = 256;
+constexpr int kRing = 4;  // K tiles in flight per wave
 
 struct PrefillPlan {
   int32_t chunk;                      // tokens per chunk (multiple of 16)
@@ -203,7 +225,8 @@ struct PrefillPlan {
 
 template <int FMT, int HT>
 __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, PrefillPlan plan) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
   const int b = blockIdx.y;
   // unit -> (chunk c, row block qb): binary search of the prefix table (scalar).
   const int u = blockIdx.x;
@@ -214,14 +237,25 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
   }
   const int c = lo;
   const int qb = plan.n_qb - 1 - (u - plan.unit_start[c]);  // heaviest row blocks first
-  const int n_b = min(max(a.ctx[b], 0), a.max_ctx);
   const int j0 = qb * kPrefillRowsPerBlock + wave * kPrefillRowsPerWave;
   if (j0 >= a.n_q) return;
-  const int j_last = min(j0 + kPrefillRowsPerWave, a.n_q) - 1;
-  const int t_end = min(valid_len(n_b, a.n_q, j_last), (c + 1) * plan.chunk);
+  const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
+  const int j_last = std::min(j0 + kPrefillRowsPerWave, a.n_q) - 1;
+  const int t_end = std::min(valid_len(n_b, a.n_q, j_last), (c + 1) * plan.chunk);
   const int t_begin = c * plan.chunk;
   if (t_begin >= t_end) return;
-  const int P = a.pool.page_size;
+  const int P = a.pool.page_size, lgP = a.pool.page_shift;
+  const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
+  const int last_page = (t_end - 1) >> lgP;
+
+  // Page ids of the unit's pages, one per lane (a chunk spans at most 64 pages).
+  const int page0 = t_begin >> lgP;
+  const int32_t win = ptb[std::min(page0 + lane, last_page)];
+  auto tile_page = [&](int s0) -> const uint8_t* {  // s0 < t_end
+    const int32_t pid = __builtin_amdgcn_readlane(win, (s0 >> lgP) - page0);
+    const bool valid_page = pid >= 0 && (int64_t)pid < a.pool.num_pages;
+    return valid_page ? a.pool.base + (int64_t)pid * a.pool.stride : nullptr;
+  };
 
   v8i qa[kPrefillRowsPerWave][HT];
   uint32_t qs[kPrefillRowsPerWave][HT];
@@ -229,7 +263,7 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
   int nv[kPrefillRowsPerWave];
 #pragma unroll
   for (int g = 0; g < kPrefillRowsPerWave; ++g) {
-    const int j = min(j0 + g, a.n_q - 1);
+    const int j = std::min(j0 + g, a.n_q - 1);
     const int64_t r = (int64_t)b * a.n_q + j;
     nv[g] = (j0 + g < a.n_q) ? valid_len(n_b, a.n_q, j0 + g) : 0;
 #pragma unroll
@@ -240,40 +274,44 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
   }
   // the valid length this lane's output column belongs to after the transpose
   const int my_n = nv[lane >> 4];
-  float* out_row = a.logits + ((int64_t)b * a.n_q + min(j0 + (lane >> 4), a.n_q - 1)) * a.lstride;
-
+  float* out_row = a.logits + ((int64_t)b * a.n_q + std::min(j0 + (lane >> 4), a.n_q - 1)) * a.lstride;
   const float qnan = __builtin_nanf("");
-  // Software pipeline: the next tile's operands load while this tile computes.
-  int s0 = t_begin;
-  Page pg = page_of(a, b, s0);
-  KTile<FMT> cur;
-  if (pg.base) cur = load_k_tile<FMT>(pg.base, P, s0 % P, lane);
-  bool cur_ok = pg.base != nullptr;
-  for (; s0 < t_end; s0 += 16) {
-    KTile<FMT> nxt;
-    bool nxt_ok = false;
-    const int s1 = s0 + 16;
-    if (s1 < t_end) {
-      const Page pn = page_of(a, b, s1);
-      if (pn.base) {
-        nxt = load_k_tile<FMT>(pn.base, P, s1 % P, lane);
-        nxt_ok = true;
+
+  // A ring of kRing tiles in flight: slot i always holds tile base + 16*i of the current
+  // round; after slot i is consumed it is refilled with the same slot of the next round.
+  // The ring index is static (fully unrolled), so no register copy ever touches a tile
+  // whose load is still in flight.
+  KTile<FMT> ring[kRing];
+  bool rok[kRing];
+  auto fetch = [&](int s, KTile<FMT>& t, bool& okk) {
+    const uint8_t* pg = (s < t_end) ? tile_page(s) : nullptr;
+    okk = pg != nullptr;
+    t = load_k_tile<FMT>(pg ? pg : a.pool.base, P, pg ? (s & (P - 1)) : 0, lane);
+  };
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) fetch(t_begin + 16 * i, ring[i], rok[i]);
+  for (int base = t_begin; base < t_end; base += 16 * kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int s0 = base + 16 * i;
+      if (s0 < t_end) {  // uniform
+        float p[kPrefillRowsPerWave];
+#pragma unroll
+        for (int g = 0; g < kPrefillRowsPerWave; ++g) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc = relu_dot_acc(mfma<FMT>(qa[g][ht], qs[g][ht], ring[i]), qw[g][ht], acc,
+                                                              ht == 0);
+          p[g] = acc;
+        }
+        float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
+        if (FMT == 1) logit *= __uint_as_float(ring[i].scale);
+        if (!rok[i]) logit = qnan;
+        const int s = s0 + (lane & 15);
+        if (s < my_n) out_row[s] = logit;
       }
+      fetch(s0 + 16 * kRing, ring[i], rok[i]);
     }
-    float p[kPrefillRowsPerWave];
-#pragma unroll
-    for (int g = 0; g < kPrefillRowsPerWave; ++g) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc += relu_dot(mfma<FMT>(qa[g][ht], qs[g][ht], cur), qw[g][ht]);
-      if (FMT == 1) acc *= __uint_as_float(cur.scale);
-      p[g] = cur_ok ? acc : qnan;
-    }
-    const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
-    const int s = s0 + (lane & 15);
-    if (s < my_n) out_row[s] = logit;
-    cur = nxt;
-    cur_ok = nxt_ok;
   }
 }
 
@@ -286,6 +324,8 @@ hipError_t launch_decode(const LogitsArgs& a, int nt, hipStream_t s) {
   case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N>), grid, dim3(256), 0, s, a); break;
     IDX_DECODE_CASE(1) IDX_DECODE_CASE(2) IDX_DECODE_CASE(3) IDX_DECODE_CASE(4)
     IDX_DECODE_CASE(5) IDX_DECODE_CASE(6) IDX_DECODE_CASE(7) IDX_DECODE_CASE(8)
+    IDX_DECODE_CASE(9) IDX_DECODE_CASE(10) IDX_DECODE_CASE(11) IDX_DECODE_CASE(12)
+    IDX_DECODE_CASE(13) IDX_DECODE_CASE(14) IDX_DECODE_CASE(15) IDX_DECODE_CASE(16)
 #undef IDX_DECODE_CASE
     default: return hipErrorInvalidValue;
   }
@@ -298,6 +338,7 @@ bool build_prefill_plan(const LogitsArgs& a, PrefillPlan& plan) {
   plan.n_qb = (a.n_q + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock;
   int chunk = 1024;
   while ((a.max_ctx + chunk - 1) / chunk > kMaxChunks) chunk *= 2;
+  if (chunk > 64 * a.pool.page_size) return false;  // rejected by the API layer first
   plan.chunk = chunk;
   plan.n_chunks = (a.max_ctx + chunk - 1) / chunk;
   if (plan.n_chunks == 0) return false;
@@ -339,12 +380,21 @@ hipError_t launch_prefill(const LogitsArgs& a, int ht, hipStream_t s) {
 
 }  // namespace
 
+bool logits_uses_decode_kernel(int n_q, int H) {
+  return n_q * ((H + kHeadTile - 1) / kHeadTile) <= kDecodeMaxTiles;
+}
+
+int64_t logits_max_ctx(int n_q, int H, int page_size) {
+  if (logits_uses_decode_kernel(n_q, H)) return INT32_MAX;
+  // prefill units span one chunk of at most 64 pages, with at most kMaxChunks chunks
+  return (int64_t)kMaxChunks * std::min(64 * page_size, 1 << 30);
+}
+
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t s) {
   if (a.max_ctx == 0) return hipSuccess;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
-  const int nt = a.n_q * ht;
-  if (nt <= kDecodeMaxTiles)
-    return a.pool.kv_format == 0 ? launch_decode<0>(a, nt, s) : launch_decode<1>(a, nt, s);
+  if (logits_uses_decode_kernel(a.n_q, a.H))
+    return a.pool.kv_format == 0 ? launch_decode<0>(a, a.n_q * ht, s) : launch_decode<1>(a, a.n_q * ht, s);
   return a.pool.kv_format == 0 ? launch_prefill<0>(a, ht, s) : launch_prefill<1>(a, ht, s);
 }
 

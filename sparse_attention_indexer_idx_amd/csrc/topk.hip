@@ -66,12 +66,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     return;
   }
   const float* row = a.logits + r * a.lstride;
+  // Branch-free loads at an in-bounds index (cells past n read cell n-1 and are masked),
+  // so all EPT loads are in flight together.
+  float raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) raw[e] = row[min(e * NT + tid, n - 1)];
   uint32_t key[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = e * NT + tid;
-    key[e] = (i < n) ? float_key(row[i]) : 0u;
-  }
+  for (int e = 0; e < EPT; ++e) key[e] = (e * NT + tid < n) ? float_key(raw[e]) : 0u;
 
   // ---- radix select of the k-th largest key ----
   uint32_t prefix = 0, pmask = 0;

@@ -88,6 +88,7 @@ def test_logits_argument_checks(lib, kw, want):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(page_size=48 + 1), bd.IDX_EUNSUPPORTED),
+    (dict(page_size=48), bd.IDX_EUNSUPPORTED),                   # a multiple of 16, not a power of two
     (dict(page_size=8), bd.IDX_EUNSUPPORTED),
     (dict(page_size=2048, page_stride_bytes=68 * 2048), bd.IDX_EUNSUPPORTED),
     (dict(page_stride_bytes=68 * 64 - 256), bd.IDX_EINVAL),     # smaller than a page
