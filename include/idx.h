@@ -183,8 +183,9 @@ int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_sc
  * a top-k index buffer).  For row r with valid length n_r (rule above):
  *   n_r <= k: out_idx[r][0..n_r) = 0..n_r-1, the rest -1;
  *   n_r >  k: the k token indices with the largest logits, equal logits broken
- *             toward the smaller index (-0.0 equals +0.0), written in ascending index
- *             order.
+ *             toward the smaller index (-0.0 equals +0.0).  The order of the k indices
+ *             within the row is unspecified but deterministic (the same input gives the
+ *             same bytes).
  * Only cells s < n_r are read.  NaN logits are outside the contract.
  * logits   device fp32 [B * n_q][logits_stride]; ctx_lens device int32 [B];
  * max_ctx  host upper bound of ctx_lens, <= logits_stride; k >= 1;

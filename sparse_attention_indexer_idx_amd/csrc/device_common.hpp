@@ -89,6 +89,19 @@ __device__ __forceinline__ void swap16(float& x, float& y) {
   y = __uint_as_float(r[1]);
 }
 
+// Inclusive prefix sum of an int over the 64 lanes of a wave, in lane order: DPP row
+// shifts by 1, 2, 4, 8 scan each row of 16 lanes, then row_bcast:15 / row_bcast:31 carry
+// the row totals into the following rows.  All VALU, no LDS round trip.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Four partial sums p_t (t = 0..3) per lane, where lane (g = lane/16, c = lane%16)
 // holds the part of column c contributed by head group g.  Returns, in lane (g, c),
 // the full sum over the four head groups of p_g at column c: the head reduction and

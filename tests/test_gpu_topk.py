@@ -34,6 +34,9 @@ def gpu_topk(logits_d, ctx, B, n_q, max_ctx, k):
     (4, 1, (65536, 65536), 1024, False),     # the longest supported row
     (5, 1, (300, 301), 7, True),             # small k
     (4, 2, (0, 3), 4, False),                # empty and tiny rows
+    (1100, 1, (1024, 5000), 1024, True),     # 256-thread variant, ties in the boundary bucket
+    (700, 1, (1000, 4096), 300, False),      # short rows, small k
+    (600, 1, (1000, 9000), 1024, False),     # 512-thread variant, 32 cells per thread
 ])
 def test_topk_isolated_exact(rows, n_q, lens, k, ties):
     rng = np.random.default_rng(rows * 7 + k + int(ties))
@@ -42,14 +45,16 @@ def test_topk_isolated_exact(rows, n_q, lens, k, ties):
     stride = int(ctx.max()) + 5
     lg = wl.random_logits(rng, B * n_q, stride, ties=ties)
     G.say(f"topk isolated rows={B * n_q} n_q={n_q} ctx={lens} k={k} ties={ties}")
-    got = gpu_topk(G.dev(lg), ctx, B, n_q, int(ctx.max()), k)
+    lg_d = G.dev(lg)
+    got = gpu_topk(lg_d, ctx, B, n_q, int(ctx.max()), k)
+    again = gpu_topk(lg_d, ctx, B, n_q, int(ctx.max()), k)
+    assert np.array_equal(got, again), "top-k output must be deterministic"
     ref = oracle.topk(lg, ctx, n_q, k)
     for r in range(B * n_q):
         g, o = got[r], ref[r]
         assert np.array_equal(np.sort(g[g >= 0]), np.sort(o[o >= 0])), f"row {r}"
         m = int((o >= 0).sum())
         assert np.all(g[m:] == -1) and np.all(g[:m] >= 0)
-        assert np.all(np.diff(g[:m]) > 0)  # ascending index order
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 3])
@@ -91,3 +96,90 @@ def test_score_plus_topk_large_pool_sampled(fmt):
     ref = G.oracle_logits(d["hp"], d["q"], d["qs"], d["w"], rows, W.max_ctx)
     tau = 1e-4 * np.nanmax(np.abs(ref))
     G.assert_topk_valid(got_all[rows], ref, W, rows, W.topk, tau, f"cfg4/fmt{fmt}")
+
+
+@pytest.mark.parametrize("rows,n,k,values", [
+    (4, 8192, 1024, (1.0,)),              # every cell equal: pure index order
+    (4, 8192, 1024, (0.0, -0.0, 2.0)),    # signed zeros tie; the boundary bucket holds ~5000 keys
+    (300, 4096, 1000, (3.0, -1.0)),       # 512-thread variant, overflowing bucket
+    (2, 16384, 1024, (5.0, 5.0, -7.5, 1e-30)),
+])
+def test_topk_bucket_overflow_exact(rows, n, k, values):
+    """Rows whose boundary bucket holds more keys than the LDS list: the register
+    fallback must give exactly the oracle's set (ties to the smaller index)."""
+    rng = np.random.default_rng(rows + n + k)
+    vals = np.array(values, np.float32)
+    lg = vals[rng.integers(0, vals.size, size=(rows, n))]
+    ctx = np.full(rows, n, np.int32)
+    G.say(f"topk overflow rows={rows} n={n} k={k} values={values}")
+    got = gpu_topk(G.dev(lg), ctx, rows, 1, n, k)
+    ref = oracle.topk(lg, ctx, 1, k)
+    for r in range(rows):
+        assert np.array_equal(np.sort(got[r]), np.sort(ref[r])), f"row {r}"
+
+
+@pytest.mark.parametrize("rows,n,k,lo,hi,step", [
+    (8, 15900, 1024, 1.0, 2.0, 0),     # bucket ~1000 keys: either side of the ranking list's size
+    (1100, 2000, 1024, 1.0, 2.0, 0),   # 256 threads, bucket ~130: one candidate per thread
+    (1100, 6000, 1024, 1.0, 2.0, 0),   # 256 threads, bucket ~380: two sweeps
+    (400, 7000, 1024, 1.0, 2.0, 0),    # 512 threads, bucket ~875: two sweeps
+    (400, 16000, 1024, 1.0, 2.0, 0),   # 512 threads, bucket ~2000: the register fallback
+    (16, 3000, 100, 1.0, 1.001, 0),    # every key in one digit: the register fallback
+    (16, 1000, 999, -1.0, 1.0, 0),     # k one below n
+    (16, 4096, 1024, 1.0, 2.0, 2.0 ** -11),  # bucket ~260 keys on 128 values: ties in a ranked bucket
+])
+def test_topk_bucket_sizes_exact(rows, n, k, lo, hi, step):
+    """Boundary buckets of chosen sizes (uniform values in [lo, hi), optionally
+    rounded to a grid): the ranked bucket, its lane-group split and the fallback all
+    give the oracle's set."""
+    rng = np.random.default_rng(rows * 3 + n + k)
+    lg = rng.uniform(lo, hi, size=(rows, n)).astype(np.float32)
+    if step:
+        lg = (np.floor(lg / step) * step).astype(np.float32)
+    ctx = np.full(rows, n, np.int32)
+    G.say(f"topk bucket rows={rows} n={n} k={k} range=[{lo}, {hi})")
+    got = gpu_topk(G.dev(lg), ctx, rows, 1, n, k)
+    ref = oracle.topk(lg, ctx, 1, k)
+    for r in range(rows):
+        assert np.array_equal(np.sort(got[r]), np.sort(ref[r])), f"row {r}"
+
+
+def test_graph_replay_matches_eager():
+    """K store + scorer + top-k captured in a HIP graph: every replay (with eager work and
+    synchronisation between replays) reproduces the eager results byte for byte."""
+    torch = G.torch_cuda()
+    W = wl.make_workload(3)
+    d = setup_scorer(W, wl.MXFP4)
+    pool = d["pool"]
+    k = G.bf16_dev(W.k_rows)
+    gam, pos, cs, sl = G.dev(W.gamma), G.dev(W.positions), G.dev(W.cos_sin), G.dev(W.slots)
+    logits = torch.zeros((W.rows, W.max_ctx), dtype=torch.float32, device="cuda")
+    out = torch.zeros((W.rows, W.topk), dtype=torch.int32, device="cuda")
+
+    def step():
+        bd.idx_k_store_mxfp4(pool.view, k, gam, W.eps, pos, cs, sl)
+        bd.idx_logits_paged(pool.view, d["q_d"], d["qs_d"], d["w_d"], d["pt_d"], d["ctx_d"], W.B, W.n_q, W.H,
+                            W.max_ctx, logits)
+        bd.idx_topk(logits, d["ctx_d"], W.B, W.n_q, W.max_ctx, W.topk, out)
+
+    G.say("graph replay cfg=3")
+    step()
+    torch.cuda.synchronize()
+    ref_pool, ref_logits, ref_out = pool.base.clone(), logits.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        logits.zero_()  # the state the eager reference started from (masked cells stay 0)
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bool((pool.base == ref_pool).all()), f"replay {rep}: pool"
+        assert torch.equal(logits.view(torch.int32), ref_logits.view(torch.int32)), f"replay {rep}: logits"
+        assert torch.equal(out, ref_out), f"replay {rep}: top-k"
