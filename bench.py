@@ -9,8 +9,14 @@ the shapes of the pages' isolated-scorer workloads, resident in HBM before timin
 
 By default the pool is rotated over enough replicas that every step reads its K cache
 from HBM rather than from the 256 MB last-level cache ("cold"); --warm uses one pool.
-Prints one JSON line.  Kernel durations come from HIP events recorded on the stream
-the kernels run on, inside the timed loop.
+Prints one JSON line.  Times come from HIP events recorded on the stream the kernels
+run on.  While the host enqueues a timed region a spin kernel holds the GPU, so the
+region runs back to back and its events measure GPU time, not host launch gaps.  Each
+kernel's duration is the mean over K back-to-back launches of that kernel alone (one
+event pair around them).  `value` is the GPU time per step of the step replayed as a
+HIP graph; the eager step and the graph's host wall time are reported beside it.
+
+    python bench.py --summarize DIR...   # tables from rocprofv3 csv output
 """
 from __future__ import annotations
 
@@ -44,6 +50,14 @@ def parse():
                     help="report the eager step time as the value (default: HIP-graph replay of the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB three times (a plain copy of "
+                         "known size that scales the memory-traffic counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print per-kernel tables from rocprofv3 csv output directories and exit")
+    ap.add_argument("--traffic-key", help="with --summarize: record the scorer's copy-scaled "
+                                          "FETCH_SIZE + WRITE_SIZE per launch under this key in profiles/traffic.json")
+    ap.add_argument("--calib-mib", type=int, default=0, help="with --traffic-key: the size of the calibration copy")
     return ap.parse_args()
 
 
@@ -102,6 +116,91 @@ def traffic_from_profiles(kernel_key, src_hash):
     return None
 
 
+SCORER_SOURCES = ("logits.hip", "device_common.hpp", "launch.hpp")
+
+
+def scorer_source_hash():
+    return source_hash([os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in SCORER_SOURCES])
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"((?:\w+::)*\w+(?:<[^()]*>)?)\(", name.replace("(anonymous namespace)::", ""))
+    return (m.group(1) if m else name).split("::")[-1]
+
+
+def summarize(dirs, traffic_key=None, calib_mib=0):
+    """Markdown tables from rocprofv3 csv output: kernel-trace statistics and, for
+    counter runs, the mean of each counter per (kernel, grid size).  With a traffic key,
+    the scorer's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counters read for the calibration copy of calib_mib MiB, and stored per launch."""
+    import csv
+    import glob
+    import collections
+    counters = collections.defaultdict(list)
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "*kernel_stats.csv"))):
+            print(f"\nkernel trace ({f}):\n")
+            print("| kernel | calls | avg µs | min µs | max µs | % of GPU time |\n|---|---|---|---|---|---|")
+            for r in csv.DictReader(open(f)):
+                print(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+        for f in sorted(glob.glob(os.path.join(d, "*kernel_trace.csv"))):
+            # bench.py times each kernel alone over K back-to-back launches; the longest
+            # run of consecutive dispatches of one kernel is that loop
+            rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+            best = {}
+            i = 0
+            while i < len(rows):
+                j = i
+                while j + 1 < len(rows) and rows[j + 1]["Kernel_Name"] == rows[i]["Kernel_Name"]:
+                    j += 1
+                name = _short_kernel(rows[i]["Kernel_Name"])
+                if j - i + 1 > best.get(name, (0,))[0]:
+                    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[i:j + 1]]
+                    best[name] = (j - i + 1, float(np.mean(dur)), float(np.median(dur)))
+                i = j + 1
+            print(f"\nlongest back-to-back run per kernel ({f}):\n")
+            print("| kernel | launches in the run | mean µs | median µs |\n|---|---|---|---|")
+            for name, (cnt, mean, med) in sorted(best.items(), key=lambda t: -t[1][0]):
+                if cnt >= 10:
+                    print(f"| `{name}` | {cnt} | {mean:.2f} | {med:.2f} |")
+        for f in sorted(glob.glob(os.path.join(d, "*counter_collection.csv"))):
+            for r in csv.DictReader(open(f)):
+                key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])
+                counters[key].append(float(r["Counter_Value"]))
+    if counters:
+        print("\n| kernel (grid threads) | counter | dispatches | mean per dispatch |\n|---|---|---|---|")
+        for (k, g, c), v in sorted(counters.items()):
+            print(f"| `{k}` ({g}) | {c} | {len(v)} | {np.mean(v):.6g} |")
+    if not traffic_key:
+        return
+    def pick(pred, counter, reduce):
+        vals = [(g, np.mean(v), max(v)) for (k, g, c), v in counters.items() if pred(k) and c == counter]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the requested kernel")
+        return reduce(vals)
+    scorer = lambda k: k.startswith("logits_")
+    copy = lambda k: "copyBuffer" in k
+    big = lambda vals: max(vals, key=lambda t: t[2])  # the largest grid = the timed launches
+    _, fetch, _ = pick(scorer, "FETCH_SIZE", big)
+    _, write, _ = pick(scorer, "WRITE_SIZE", big)
+    known_kib = calib_mib * 1024.0
+    f_fetch = known_kib / pick(copy, "FETCH_SIZE", lambda v: max(t[2] for t in v))
+    f_write = known_kib / pick(copy, "WRITE_SIZE", lambda v: max(t[2] for t in v))
+    entry = {"fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+             "copy_scale_fetch": round(f_fetch, 4), "copy_scale_write": round(f_write, 4),
+             "hbm_bytes_per_launch": int(round((fetch * f_fetch + write * f_write) * 1024)),
+             "source_hash": scorer_source_hash()}
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(p)) if os.path.exists(p) else {}
+    d[traffic_key] = entry
+    with open(p, "w") as fh:
+        json.dump(d, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(f"\n{traffic_key}: {json.dumps(entry)}")
+
+
 def cpu_baseline(W, fmt, budget_s):
     """The oracle, as it stands, on the host cores: one full step (K store of the new
     rows, logits of every row, top-k of every row) for the decode workloads; for the
@@ -151,6 +250,9 @@ def cpu_baseline(W, fmt, budget_s):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.traffic_key, args.calib_mib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
         sys.exit(2)
@@ -205,76 +307,123 @@ def main():
     out = torch.empty((W.rows, W.topk), dtype=torch.int32, device="cuda")
     new = step_rows(W)
     k_new, pos_new, slot_new = k_all[dev(new)], positions[dev(new)], slots[dev(new)]
+    if args.calib_copy_mib:  # a plain device copy of known size, outside the timed region
+        src = torch.ones((args.calib_copy_mib << 20,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
-        pv = pools[i % replicas][1]
-        if ev:
-            ev[0].record()
-        store(pv, k_new, gamma, W.eps, pos_new, cos_sin, slot_new)
-        if ev:
-            ev[1].record()
-        bd.idx_logits_paged(pv, q, qs, w, pt, ctx, W.B, W.n_q, W.H, W.max_ctx, logits)
-        if ev:
-            ev[2].record()
+    def k_store(i):
+        store(pools[i % replicas][1], k_new, gamma, W.eps, pos_new, cos_sin, slot_new)
+
+    def score(i):
+        bd.idx_logits_paged(pools[i % replicas][1], q, qs, w, pt, ctx, W.B, W.n_q, W.H, W.max_ctx, logits)
+
+    def topk(i):
         bd.idx_topk(logits, ctx, W.B, W.n_q, W.max_ctx, W.topk, out)
-        if ev:
-            ev[3].record()
+
+    def step(i):
+        k_store(i)
+        score(i)
+        topk(i)
+
+    def held(fn, n, host_s):
+        """GPU time of n back-to-back calls fn(0..n-1): a spin kernel holds the GPU while
+        the host enqueues them, and one event pair brackets the whole run, so neither
+        host launch gaps nor per-call event overhead enter the average.  Returns the mean
+        per call and the means of groups of 10 calls (µs)."""
+        torch.cuda.synchronize()
+        groups = max(1, n // 10)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+        torch.cuda._sleep(int((2.0 * host_s * n + 2e-3) * 2.4e9))
+        ev[0].record()
+        for gi in range(groups):
+            for i in range(gi * n // groups, (gi + 1) * n // groups):
+                fn(i)
+            ev[gi + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[gi].elapsed_time(ev[gi + 1]) * 1e3 / ((gi + 1) * n // groups - gi * n // groups)
+               for gi in range(groups)]
+        return ev[0].elapsed_time(ev[-1]) * 1e3 / n, np.array(per)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: exactly K steps, events on the kernels' own (current) stream
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    h0 = time.perf_counter()
+    for i in range(args.warmup):
+        step(i)
+    host_s = (time.perf_counter() - h0) / max(args.warmup, 1)  # host cost of enqueueing one step
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eager_ms = (t1 - t0) * 1e3 / args.steps
-    k_us = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e3
-    s_us = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e3
-    t_us = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e3
+    # Timed region: exactly K eager steps on the kernels' own (current) stream, then each
+    # kernel alone K times back to back for its average duration.
+    eager_us, _ = held(step, args.steps, host_s)
+    eager_ms = eager_us * 1e-3
+    k_mean, k_us = held(k_store, args.steps, host_s)
+    s_mean, s_us = held(score, args.steps, host_s)
+    t_mean, t_us = held(topk, args.steps, host_s)
 
-    # The same step captured once per pool replica into a HIP graph and replayed, as a
-    # serving loop runs the indexer; the timed region is exactly K replays.
-    graphs = []
+    # The step captured into HIP graphs, as a serving loop runs the indexer inside a
+    # captured forward pass: graph A holds L consecutive steps (L a multiple of the replica
+    # count, at least 8, so a replay's fixed launch cost is shared as it is across the
+    # layers of a captured model), graph B the K mod L remaining ones; the timed region is
+    # exactly K steps.
+    L = replicas * max(1, -(-8 // replicas))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(replicas):
+        for i in range(L):
             step(i)  # warm the captured configuration eagerly on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for i in range(replicas):
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % replicas].replay()
+            for i in range(n):
+                step(i)
+        return g
+    graph_a = capture(L)
+    rem = args.steps % L
+    graph_b = capture(rem) if rem else None
+
+    def replay_k():
+        for _ in range(args.steps // L):
+            graph_a.replay()
+        if graph_b is not None:
+            graph_b.replay()
+    replay_k()  # warm-up replays (untimed)
     torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    replay_k()
+    host_s = (time.perf_counter() - h0) / args.steps
+    torch.cuda.synchronize()
+    # GPU time of K steps (the host enqueues the replays while a spin kernel holds the
+    # GPU), and separately the wall time of K steps enqueued as the host goes.
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int((2.0 * host_s * args.steps + 2e-3) * 2.4e9))
+    g0.record()
+    replay_k()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % replicas].replay()
+    replay_k()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    graph_ms = (t1 - t0) * 1e3 / args.steps
+    graph_wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_per_step = eager_ms if args.eager else graph_ms
 
     ab = algorithmic_bytes(W, fmt, len(new))
-    src = [os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in
-           ("logits.hip", "device_common.hpp", "launch.hpp")]
-    shash = source_hash(src)
+    shash = scorer_source_hash()
     prefill = not decode_form(W)
     if prefill:
-        achieved = ab["flops"] / (s_us.mean() * 1e-6) / 1e12
+        achieved = ab["flops"] / (s_mean * 1e-6) / 1e12
         peak = FP4_PEAK_TFLOPS if fmt == 0 else FP8_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
     else:
-        achieved = ab["scorer"] / (s_us.mean() * 1e-6) / 1e9
+        achieved = ab["scorer"] / (s_mean * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["kernel"] = "logits_prefill_kernel" if prefill else "logits_decode_kernel"
@@ -296,15 +445,16 @@ def main():
         "config": {"workload": W.name, "B": W.B, "n_q": W.n_q, "H": W.H, "D": 128, "page_size": P,
                    "max_ctx": W.max_ctx, "topk": W.topk, "kv": args.kv,
                    "cache": "warm" if args.warm else f"cold ({replicas} pool replicas rotated)"},
-        "step_us": {"graph": round(graph_ms * 1e3, 3), "eager": round(eager_ms * 1e3, 3)},
-        "breakdown_us": {"k_store": round(float(np.median(k_us)), 3), "score": round(float(np.median(s_us)), 3),
-                         "topk": round(float(np.median(t_us)), 3),
+        "step_us": {"graph": round(graph_ms * 1e3, 3), "eager": round(eager_ms * 1e3, 3),
+                    "graph_wall": round(graph_wall_ms * 1e3, 3), "steps_per_graph": L},
+        "breakdown_us": {"k_store": round(k_mean, 3), "score": round(s_mean, 3), "topk": round(t_mean, 3),
                          "score_p10_p90": [round(float(np.percentile(s_us, 10)), 3),
                                            round(float(np.percentile(s_us, 90)), 3)],
-                         "score_plus_topk_mean": round(float(s_us.mean() + t_us.mean()), 3)},
+                         "score_plus_topk": round(s_mean + t_mean, 3),
+                         "note": "each kernel alone, back to back; per-call mean (p10/p90 over groups of 10 calls)"},
         "roofline": roof,
-        "topk_hbm_gbs": round(ab["topk"] / (t_us.mean() * 1e-6) / 1e9, 1),
-        "scorer_tflops": round(ab["flops"] / (s_us.mean() * 1e-6) / 1e12, 2),
+        "topk_hbm_gbs": round(ab["topk"] / (t_mean * 1e-6) / 1e9, 1),
+        "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, fmt, args.cpu_budget_s)
