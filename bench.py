@@ -276,7 +276,7 @@ def main():
     # the last-level cache holds, so only decode rotates pool replicas.
     prefill_like = not decode_form(W)
     replicas = 1 if (args.warm or prefill_like) else max(2, int(np.ceil(2 * LLC_BYTES / max(used_bytes, 1))) + 1)
-    replicas = min(replicas, 16, max(1, int((64 << 30) // pool_bytes)))
+    replicas = min(replicas, 64, max(1, int((64 << 30) // pool_bytes)))
 
     # ---- inputs in HBM ----
     k_all = dev(W.k_rows.view(np.int16)).view(torch.bfloat16)

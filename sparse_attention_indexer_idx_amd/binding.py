@@ -44,6 +44,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise OSError(f"{p} not found: build it with `python -m sparse_attention_indexer_idx_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch already loaded, so the
+    # two share one runtime (devices, streams and allocations), whatever the import order.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     V, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     PP = ctypes.POINTER(IdxPool)

@@ -45,32 +45,42 @@ struct KTile {
   uint32_t scale;
 };
 
-template <int FMT>
+// A load that is either plain or marked non-temporal (STREAM: K bytes read once per
+// call, as in decode — the hint keeps them from displacing reused lines in the caches;
+// prefill re-reads its K tiles from L2 and loads them plainly).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <bool STREAM, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if (STREAM) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <int FMT, bool STREAM>
 __device__ __forceinline__ KTile<FMT> load_k_tile(const uint8_t* __restrict__ page, int P, int row0, int lane) {
   KTile<FMT> t;
   const uint32_t tok = (uint32_t)(row0 + (lane & 15)), g = (uint32_t)(lane >> 4);
   if (FMT == 0) {
-    const uint4 x = *(const uint4*)(page + (tok * 64u + 16u * g));
+    const u32x4 x = ld<STREAM>((const u32x4*)(page + (tok * 64u + 16u * g)));
     t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-    t.scale = page[(uint32_t)P * 64u + tok * 4u + g];
+    t.scale = ld<STREAM>(page + ((uint32_t)P * 64u + tok * 4u + g));
   } else {
-    const uint4* src = (const uint4*)(page + (tok * 128u + 32u * g));
-    const uint4 x = src[0], y = src[1];
+    const u32x4* src = (const u32x4*)(page + (tok * 128u + 32u * g));
+    const u32x4 x = ld<STREAM>(src), y = ld<STREAM>(src + 1);
     t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-    t.scale = *(const uint32_t*)(page + ((uint32_t)P * 128u + tok * 4u));
+    t.scale = ld<STREAM>((const uint32_t*)(page + ((uint32_t)P * 128u + tok * 4u)));
   }
   return t;
 }
 
 // A operand for head tile `ht` of query row r: lane l -> head ht*16 + l%16, block l/16.
+// Branch-free: a head past H loads head H-1 and is zeroed by a select after the load, so
+// the loads of every tile go out together and nothing waits for them before first use.
 template <int FMT>
 __device__ __forceinline__ void load_q_tile(const LogitsArgs& a, int64_t r, int ht, int lane, v8i& v,
                                             uint32_t& sc) {
   const int h = ht * kHeadTile + (lane & 15), g = lane >> 4;
-  v = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  sc = 0;
-  if (h >= a.H) return;
-  const int64_t vec = r * a.H + h;
+  const bool hv = h < a.H;
+  const int64_t vec = r * a.H + (hv ? h : a.H - 1);
   if (FMT == 0) {
     const uint4 x = *(const uint4*)(a.q + vec * 64 + 16 * g);
     v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
@@ -81,15 +91,20 @@ __device__ __forceinline__ void load_q_tile(const LogitsArgs& a, int64_t r, int 
     v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
     sc = kE8m0One;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = hv ? v[i] : 0;
 }
 
-// Weights of the four accumulator rows lane l holds for head tile ht of row r.
+// Weights of the four accumulator rows lane l holds for head tile ht of row r (heads
+// ht*16 + 4*(l/16) + i); a head past H gets weight 0.
 __device__ __forceinline__ v4f load_w_tile(const LogitsArgs& a, int64_t r, int ht, int lane) {
+  const int h0 = ht * kHeadTile + 4 * (lane >> 4);
   v4f w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = ht * kHeadTile + 4 * (lane >> 4) + i;
-    w[i] = (h < a.H) ? a.w[r * a.H + h] : 0.0f;
+    const int h = h0 + i;
+    const float x = a.w[r * a.H + (h < a.H ? h : a.H - 1)];
+    w[i] = h < a.H ? x : 0.0f;
   }
   return w;
 }
@@ -128,46 +143,30 @@ __device__ __forceinline__ float relu_dot(const v4f& d, const v4f& w) {
 
 // ------------------------------------------------------------------------------------
 // Decode: every query row of a sequence in registers (n_q * ceil(H/16) <= 16 head
-// tiles), one wave per 64 consecutive cached tokens (four 16-token tiles), 4 waves per
-// block; grid = (ceil(max_ctx / 256), B).  Per wave: the page ids of its four tiles and
-// the sequence length are fetched together, then all K, Q and weight loads are issued
-// before the first use.
+// tiles), one wave per G*64 consecutive cached tokens (G groups of four 16-token tiles),
+// 4 waves per block; grid = (ceil(max_ctx / (256*G)), B).  Per wave: Q and w loads, then
+// the page ids of its tiles and the sequence length together, then all K loads, before
+// the first use.
 // ------------------------------------------------------------------------------------
 constexpr int kDecodeMaxTiles = 16;
-constexpr int kDecodeTokPerWave = 64;
 constexpr int kDecodeWaves = 4;
 
-template <int FMT, int NT>
+template <int FMT, int NT, int G>
 __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
+  constexpr int T = 4 * G;  // K tiles per wave
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int b = blockIdx.y;
-  const int tok0 = (blockIdx.x * kDecodeWaves + wave) * kDecodeTokPerWave;
-  if (tok0 >= a.max_ctx) return;
+  const int tok0 = (blockIdx.x * kDecodeWaves + wave) * (16 * T);
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int last_page = (a.max_ctx - 1) >> lgP;
   const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
 
-  int32_t pid[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) pid[t] = uniform(ptb[std::min((tok0 + 16 * t) >> lgP, last_page)]);
-  const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
-  if (tok0 >= n_b) return;
-
-  // K tiles: a tile past the sequence end or on an invalid page reads page 0 row 0
-  // (always inside the pool) and is masked below.
-  KTile<FMT> kt[4];
-  bool ok[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int s0 = tok0 + 16 * t;
-    const bool valid_page = pid[t] >= 0 && (int64_t)pid[t] < a.pool.num_pages;
-    const int64_t p = valid_page ? pid[t] : 0;
-    const uint8_t* page = a.pool.base + p * a.pool.stride;
-    kt[t] = load_k_tile<FMT>(page, P, valid_page ? (s0 & (P - 1)) : 0, lane);
-    ok[t] = valid_page;  // tiles past n_b are computed but never stored
-  }
-
+  // Q and w first: they do not depend on the page table and come from L2, so they are
+  // in registers by the time the K bytes arrive.  The kernel has no early exit: a wave
+  // past the end of the context reads page 0 row 0 for every tile (an L2 hit shared by
+  // all such waves) and stores nothing, so no branch stands between these loads and the
+  // page-table round trip.
   const int HT = (a.H + kHeadTile - 1) / kHeadTile;
   v8i qa[NT];
   uint32_t qs[NT];
@@ -180,26 +179,55 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
     qw[m] = load_w_tile(a, r, ht, lane);
   }
 
+  // The tile page ids (clamped into the sequence's table row) and the length, together.
+  int32_t pid[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) pid[t] = uniform(ptb[std::min((tok0 + 16 * t) >> lgP, last_page)]);
+  const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
+  const bool live = tok0 < n_b;  // n_b <= max_ctx, so this also covers waves past max_ctx
+
+  // K tiles: a tile of a dead wave or on an invalid page reads page 0 row 0 (always
+  // inside the pool); invalid pages score NaN below, dead waves store nothing.
+  KTile<FMT> kt[T];
+  bool ok[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int s0 = tok0 + 16 * t;
+    const bool valid_page = pid[t] >= 0 && (int64_t)pid[t] < a.pool.num_pages;
+    const bool use = live && valid_page;
+    const uint8_t* page = a.pool.base + (use ? (int64_t)pid[t] : 0) * a.pool.stride;
+    kt[t] = load_k_tile<FMT, true>(page, P, use ? (s0 & (P - 1)) : 0, lane);
+    ok[t] = valid_page;  // tiles past n_b are computed but never stored
+  }
+
   const float qnan = __builtin_nanf("");
-  const int s = tok0 + lane;
-  for (int j = 0; j < a.n_q; ++j) {
-    float p[4];
+  // Head tiles m = j*HT .. j*HT+HT-1 belong to query row j.  Every MFMA runs
+  // unconditionally (so nothing sinks the Q loads behind a branch); a row is finished —
+  // head reduction, transpose, store — once its last tile is in.  A dead wave (tok0 >= n_b)
+  // stores nothing: s >= tok0 >= n_b >= every valid length.
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float acc = 0.0f;
-      bool first = true;
+  for (int g = 0; g < G; ++g) {
+    const int s = tok0 + 64 * g + lane;
+    float acc[4];
 #pragma unroll
-      for (int m = 0; m < NT; ++m)
-        if (m / HT == j) {
-          const float v = relu_dot(mfma<FMT>(qa[m], qs[m], kt[t]), qw[m]);
-          acc = first ? v : acc + v;
-          first = false;
+    for (int m = 0; m < NT; ++m) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float v = relu_dot(mfma<FMT>(qa[m], qs[m], kt[4 * g + t]), qw[m]);
+        acc[t] = (m % HT == 0) ? v : acc[t] + v;
+      }
+      if ((m + 1) % HT == 0) {  // uniform
+        const int j = m / HT;
+        float p[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float v = FMT == 1 ? acc[t] * __uint_as_float(kt[4 * g + t].scale) : acc[t];
+          p[t] = ok[4 * g + t] ? v : qnan;
         }
-      if (FMT == 1) acc *= __uint_as_float(kt[t].scale);
-      p[t] = ok[t] ? acc : qnan;
+        const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
+        if (s < valid_len(n_b, a.n_q, j)) a.logits[((int64_t)b * a.n_q + j) * a.lstride + s] = logit;
+      }
     }
-    const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
-    if (s < valid_len(n_b, a.n_q, j)) a.logits[((int64_t)b * a.n_q + j) * a.lstride + s] = logit;
   }
 }
 
@@ -286,7 +314,7 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
   auto fetch = [&](int s, KTile<FMT>& t, bool& okk) {
     const uint8_t* pg = (s < t_end) ? tile_page(s) : nullptr;
     okk = pg != nullptr;
-    t = load_k_tile<FMT>(pg ? pg : a.pool.base, P, pg ? (s & (P - 1)) : 0, lane);
+    t = load_k_tile<FMT, false>(pg ? pg : a.pool.base, P, pg ? (s & (P - 1)) : 0, lane);
   };
 #pragma unroll
   for (int i = 0; i < kRing; ++i) fetch(t_begin + 16 * i, ring[i], rok[i]);
@@ -315,13 +343,13 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
   }
 }
 
-template <int FMT>
-hipError_t launch_decode(const LogitsArgs& a, int nt, hipStream_t s) {
-  const dim3 grid((unsigned)((a.max_ctx + kDecodeWaves * kDecodeTokPerWave - 1) / (kDecodeWaves * kDecodeTokPerWave)),
-                  (unsigned)a.B);
+template <int FMT, int G>
+hipError_t launch_decode_g(const LogitsArgs& a, int nt, hipStream_t s) {
+  const int tok_per_block = kDecodeWaves * 64 * G;
+  const dim3 grid((unsigned)((a.max_ctx + tok_per_block - 1) / tok_per_block), (unsigned)a.B);
   switch (nt) {
 #define IDX_DECODE_CASE(N) \
-  case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N>), grid, dim3(256), 0, s, a); break;
+  case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N, G>), grid, dim3(256), 0, s, a); break;
     IDX_DECODE_CASE(1) IDX_DECODE_CASE(2) IDX_DECODE_CASE(3) IDX_DECODE_CASE(4)
     IDX_DECODE_CASE(5) IDX_DECODE_CASE(6) IDX_DECODE_CASE(7) IDX_DECODE_CASE(8)
     IDX_DECODE_CASE(9) IDX_DECODE_CASE(10) IDX_DECODE_CASE(11) IDX_DECODE_CASE(12)
@@ -330,6 +358,13 @@ hipError_t launch_decode(const LogitsArgs& a, int nt, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Two 64-token groups per wave while the query tiles leave room in registers: each wave
+// then carries twice the K bytes per page-table and Q round trip.
+template <int FMT>
+hipError_t launch_decode(const LogitsArgs& a, int nt, hipStream_t s) {
+  return nt <= 4 ? launch_decode_g<FMT, 2>(a, nt, s) : launch_decode_g<FMT, 1>(a, nt, s);
 }
 
 // Host-side plan of the prefill units (assumes every sequence has max_ctx tokens;
@@ -390,8 +425,9 @@ int64_t logits_max_ctx(int n_q, int H, int page_size) {
   return (int64_t)kMaxChunks * std::min(64 * page_size, 1 << 30);
 }
 
-hipError_t launch_logits(const LogitsArgs& a, hipStream_t s) {
-  if (a.max_ctx == 0) return hipSuccess;
+hipError_t launch_logits(const LogitsArgs& args, hipStream_t s) {
+  if (args.max_ctx == 0) return hipSuccess;
+  const LogitsArgs& a = args;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
   if (logits_uses_decode_kernel(a.n_q, a.H))
     return a.pool.kv_format == 0 ? launch_decode<0>(a, a.n_q * ht, s) : launch_decode<1>(a, a.n_q * ht, s);
