@@ -152,17 +152,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   const int ne = (n + NT - 1) / NT;  // rounds that hold valid cells (uniform)
   const float* row = a.logits + r * a.lstride;
   // Branch-free loads at an in-bounds index (cells past n read cell n-1 and are masked),
-  // so all loads are in flight together.
+  // so all loads are in flight together; the histogram is cleared while they are.
   float raw[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) raw[e] = row[min(e * NT + tid, n - 1)];
+  for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
   uint32_t key[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) key[e] = (e * NT + tid < n) ? float_key(raw[e]) : 0u;
+  __syncthreads();
 
   // ---- pass 1: the top D1 bits of every valid cell ----
-  for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if (e < ne && key[e] != 0u) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
