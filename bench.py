@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="report the eager step time as the value (default: HIP-graph replay of the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the step as three calls even where the fused decode step applies")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB three times (a plain copy of "
@@ -329,6 +331,22 @@ def main():
         score(i)
         topk(i)
 
+    ws = torch.zeros((max(bd.idx_decode_step_workspace_bytes(W.B), 256) // 4,), dtype=torch.int32, device="cuda")
+
+    def fused_step(i):
+        bd.idx_decode_step(pools[i % replicas][1], k_new, gamma, W.eps, pos_new, cos_sin, slot_new, q, qs, w, pt, ctx,
+                           W.B, W.n_q, W.H, W.max_ctx, logits, W.topk, out, ws)
+
+    fused = not args.separate and len(new) == W.B * W.n_q
+    if fused:
+        try:
+            fused_step(0)
+            torch.cuda.synchronize()
+        except bd.IdxError as e:
+            if e.status != bd.IDX_EUNSUPPORTED:
+                raise
+            fused = False
+
     def held(fn, n, host_s):
         """GPU time of n back-to-back calls fn(0..n-1): a spin kernel holds the GPU while
         the host enqueues them, and one event pair brackets the whole run, so neither
@@ -370,48 +388,59 @@ def main():
     # layers of a captured model), graph B the K mod L remaining ones; the timed region is
     # exactly K steps.
     L = replicas * max(1, -(-8 // replicas))
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(L):
-            step(i)  # warm the captured configuration eagerly on the capture stream
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
 
-    def capture(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                step(i)
-        return g
-    graph_a = capture(L)
-    rem = args.steps % L
-    graph_b = capture(rem) if rem else None
+    def time_graph(step_fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(L):
+                step_fn(i)  # warm the captured configuration eagerly on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
 
-    def replay_k():
-        for _ in range(args.steps // L):
-            graph_a.replay()
-        if graph_b is not None:
-            graph_b.replay()
-    replay_k()  # warm-up replays (untimed)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    replay_k()
-    host_s = (time.perf_counter() - h0) / args.steps
-    torch.cuda.synchronize()
-    # GPU time of K steps (the host enqueues the replays while a spin kernel holds the
-    # GPU), and separately the wall time of K steps enqueued as the host goes.
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int((2.0 * host_s * args.steps + 2e-3) * 2.4e9))
-    g0.record()
-    replay_k()
-    g1.record()
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / args.steps
-    t0 = time.perf_counter()
-    replay_k()
-    torch.cuda.synchronize()
-    graph_wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    step_fn(i)
+            return g
+        graph_a = capture(L)
+        rem = args.steps % L
+        graph_b = capture(rem) if rem else None
+
+        def replay_k():
+            for _ in range(args.steps // L):
+                graph_a.replay()
+            if graph_b is not None:
+                graph_b.replay()
+        replay_k()  # warm-up replays (untimed)
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        replay_k()
+        host_s = (time.perf_counter() - h0) / args.steps
+        torch.cuda.synchronize()
+        # GPU time of K steps (the host enqueues the replays while a spin kernel holds the
+        # GPU), and separately the wall time of K steps enqueued as the host goes.
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int((2.0 * host_s * args.steps + 2e-3) * 2.4e9))
+        g0.record()
+        replay_k()
+        g1.record()
+        torch.cuda.synchronize()
+        gpu_ms = g0.elapsed_time(g1) / args.steps
+        t0 = time.perf_counter()
+        replay_k()
+        torch.cuda.synchronize()
+        return gpu_ms, (time.perf_counter() - t0) * 1e3 / args.steps
+
+    graph_ms, graph_wall_ms = time_graph(step)
+    sep_graph_ms = graph_ms
+    fused_us = None
+    if fused:
+        # The same step through the fused entry point (K store + scorer + top-k in one
+        # launch); its result equals the separate calls bit for bit (tested).
+        fused_us, _ = held(fused_step, args.steps, host_s)
+        graph_ms, graph_wall_ms = time_graph(fused_step)
     ms_per_step = eager_ms if args.eager else graph_ms
 
     ab = algorithmic_bytes(W, fmt, len(new))
@@ -446,7 +475,10 @@ def main():
                    "max_ctx": W.max_ctx, "topk": W.topk, "kv": args.kv,
                    "cache": "warm" if args.warm else f"cold ({replicas} pool replicas rotated)"},
         "step_us": {"graph": round(graph_ms * 1e3, 3), "eager": round(eager_ms * 1e3, 3),
-                    "graph_wall": round(graph_wall_ms * 1e3, 3), "steps_per_graph": L},
+                    "graph_wall": round(graph_wall_ms * 1e3, 3), "steps_per_graph": L,
+                    "path": "fused idx_decode_step" if fused else "idx_k_store + idx_logits_paged + idx_topk",
+                    "separate_graph": round(sep_graph_ms * 1e3, 3),
+                    "fused_kernel": None if fused_us is None else round(fused_us, 3)},
         "breakdown_us": {"k_store": round(k_mean, 3), "score": round(s_mean, 3), "topk": round(t_mean, 3),
                          "score_p10_p90": [round(float(np.percentile(s_us, 10)), 3),
                                            round(float(np.percentile(s_us, 90)), 3)],

@@ -194,6 +194,46 @@ int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_sc
 int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens, int32_t B, int32_t n_q,
              int32_t max_ctx, int32_t k, int32_t* out_idx, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Fused decode step: the K store of the step's new rows, the scorer and the top-k in
+ * one launch.  The pages run these as separate launches per indexer layer (page "Dense
+ * MXFP4 indexer for DeepSeek-V4 on ROCm", Changes: the K write, then the MQA-logits
+ * kernel; Purpose: top-k 1024), and at decode sizes each is dominated by launch and
+ * dependency latency.  The result equals
+ *   idx_k_store_{mxfp4|fp8}(rows 0..B*n_q-1)  then  idx_logits_paged  then  idx_topk
+ * on the same arguments (the same pool bytes, the same logits bits, the same indices),
+ * given the contract below.
+ *
+ * New rows: row i = b * n_q + j of k_bf16 / positions / slot_mapping is the K row of
+ * token t = ctx_lens[b] - n_q + j of sequence b (the sequence's newest n_q tokens, as in
+ * a decode step where ctx_lens already counts them).  A non-negative slot must be the
+ * slot the page table maps token t to: page_table[b][t / P] * P + t % P (other slots
+ * give unspecified logits for the step and may race with reads of the pool).  Rows with
+ * t < 0, a negative slot, a slot outside the pool or a position outside [0, max_pos)
+ * are not stored, exactly as idx_k_store skips them.
+ *
+ * Arguments are those of idx_k_store_* (the pool's format selects MXFP4 or FP8),
+ * idx_logits_paged and idx_topk, plus:
+ * workspace        device memory of at least idx_decode_step_workspace_bytes(B) bytes,
+ *                  4-byte aligned, zero-filled before its first use; every call leaves
+ *                  it zero again.  Calls that share a workspace must not overlap.
+ * Supported shapes (else IDX_EUNSUPPORTED, before anything is enqueued): n_q * ceil(H/16)
+ * <= 2 and max_ctx <= 16384.
+ * Execution: one kernel of 1024-thread blocks, each scoring 2048 tokens of a sequence;
+ * when that grid (ceil(max_ctx / 2048) * B blocks) exceeds the device's CU count, the
+ * K store, scorer and top-k kernels run one after another instead, with the same
+ * results (the fused launch pays off only while every block has a CU to itself).
+ * ------------------------------------------------------------------------------- */
+int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
+                    float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                    const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                    const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
+                    int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
+                    int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes idx_decode_step needs for B sequences (a multiple of 256; 0 if B < 1). */
+size_t idx_decode_step_workspace_bytes(int32_t B);
+
 /* Diagnostic: quot[i] = a[i] / b[i] and root[i] = sqrt(a[i]) in fp64 on the device,
  * with the same division and square-root operations the K store uses, so a test can
  * confirm that they round exactly as IEEE-754 prescribes (the K store's bit-exactness

@@ -18,7 +18,8 @@ IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP = 0, -1, -2, -3, -4
 IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_q_quant_mxfp4", "idx_q_quant_fp8", "idx_logits_paged",
-           "idx_topk", "idx_diag_fp64", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
+           "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_bytes_per_token",
+           "idx_device_check", "idx_status_string")
 
 
 class IdxError(RuntimeError):
@@ -57,6 +58,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_q_quant_fp8": [V, V, I64, V, V, V],
         "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V],
         "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
+        "idx_decode_step": [PP, V, I64, V, F32, V, V, I32, V, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, I32,
+                            V, V, ctypes.c_size_t, V],
+        "idx_decode_step_workspace_bytes": [I32],
         "idx_diag_fp64": [V, V, V, V, I64, V],
         "idx_bytes_per_token": [I32],
         "idx_device_check": [],
@@ -67,6 +71,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int
     lib.idx_bytes_per_token.restype = ctypes.c_int64
+    lib.idx_decode_step_workspace_bytes.restype = ctypes.c_size_t
     lib.idx_status_string.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
@@ -133,6 +138,23 @@ def idx_logits_paged(pool: IdxPool, q, q_scale, w, page_table, ctx_lens, B: int,
 def idx_topk(logits, ctx_lens, B: int, n_q: int, max_ctx: int, k: int, out_idx, stream=None):
     _check("idx_topk", load().idx_topk(_ptr(logits), logits.stride(0), _ptr(ctx_lens), B, n_q, max_ctx, k,
                                        _ptr(out_idx), _stream(stream)))
+
+
+def idx_decode_step_workspace_bytes(B: int) -> int:
+    return int(load().idx_decode_step_workspace_bytes(B))
+
+
+def idx_decode_step(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin, slot_mapping, q, q_scale, w,
+                    page_table, ctx_lens, B: int, n_q: int, H: int, max_ctx: int, logits, k: int, out_idx, workspace,
+                    stream=None):
+    """k_bf16 / positions / slot_mapping hold the B*n_q new rows (row b*n_q + j is token
+    ctx[b] - n_q + j of sequence b); workspace is a zero-filled device buffer of at least
+    idx_decode_step_workspace_bytes(B) bytes."""
+    _check("idx_decode_step", load().idx_decode_step(
+        ctypes.byref(pool), _ptr(k_bf16), k_bf16.stride(0), _ptr(gamma), eps, _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(slot_mapping), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1],
+        _ptr(ctx_lens), B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), k, _ptr(out_idx), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def idx_diag_fp64(a, b, quot, root, stream=None):

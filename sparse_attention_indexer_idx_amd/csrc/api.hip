@@ -38,6 +38,27 @@ int check_device() {
   return ok ? IDX_OK : IDX_EUNSUPPORTED;
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int num_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 int64_t bytes_per_token(int32_t fmt) { return fmt == IDX_KV_MXFP4 ? 68 : (fmt == IDX_KV_FP8_E4M3 ? 132 : -1); }
 
 // Pool checks shared by every entry point that takes a pool.
@@ -132,10 +153,12 @@ IDX_EXPORT int idx_q_quant_fp8(const void* q_bf16, const float* w, int64_t n_vec
                                             static_cast<hipStream_t>(stream)));
 }
 
-IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
-                                const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
-                                int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
-                                int64_t logits_stride, void* stream) {
+namespace {
+
+// Scorer argument checks shared by idx_logits_paged and idx_decode_step.
+int logits_args(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B, int32_t n_q,
+                int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride, idx::LogitsArgs& a) {
   int st = check_pool(pool, -1);
   if (st != IDX_OK) return st;
   if (D != 128) return IDX_EUNSUPPORTED;
@@ -148,8 +171,6 @@ IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const ui
   if ((reinterpret_cast<uintptr_t>(q) & 15u) != 0) return IDX_EALIGN;
   if ((int64_t)B * n_q > (int64_t)INT32_MAX) return IDX_EINVAL;
   if ((int64_t)max_ctx > idx::logits_max_ctx(n_q, H, pool->page_size)) return IDX_EUNSUPPORTED;
-  if ((st = check_device()) != IDX_OK) return st;
-  idx::LogitsArgs a;
   a.pool = view_of(pool);
   a.q = q;
   a.q_scale = q_scale;
@@ -163,6 +184,20 @@ IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const ui
   a.max_ctx = max_ctx;
   a.logits = logits;
   a.lstride = logits_stride;
+  return IDX_OK;
+}
+
+}  // namespace
+
+IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                                const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
+                                int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
+                                int64_t logits_stride, void* stream) {
+  idx::LogitsArgs a;
+  int st = logits_args(pool, q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, max_ctx, logits,
+                       logits_stride, a);
+  if (st != IDX_OK) return st;
+  if ((st = check_device()) != IDX_OK) return st;
   return hip_status(idx::launch_logits(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -185,6 +220,42 @@ IDX_EXPORT int idx_topk(const float* logits, int64_t logits_stride, const int32_
   a.k = k;
   a.out = out_idx;
   return hip_status(idx::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT size_t idx_decode_step_workspace_bytes(int32_t B) {
+  if (B < 1) return 0;
+  return ((size_t)B * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+IDX_EXPORT int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
+                               float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                               const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                               const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
+                               int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
+                               int64_t logits_stride, int32_t k, int32_t* out_idx, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  idx::StepArgs a;
+  int st = logits_args(pool, q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, max_ctx, logits,
+                       logits_stride, a.s);
+  if (st != IDX_OK) return st;
+  if (!k_bf16 || !gamma || !positions || !cos_sin || !slot_mapping || !out_idx || !workspace) return IDX_EINVAL;
+  if (row_stride_elems < 128 || !(eps > 0.0f) || max_pos <= 0 || k < 1) return IDX_EINVAL;
+  if (workspace_bytes < idx_decode_step_workspace_bytes(B)) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return IDX_EALIGN;
+  if (!idx::decode_step_supported(n_q, H, max_ctx)) return IDX_EUNSUPPORTED;
+  if ((st = check_device()) != IDX_OK) return st;
+  a.k = static_cast<const uint16_t*>(k_bf16);
+  a.row_stride = row_stride_elems;
+  a.gamma = gamma;
+  a.eps = (double)eps;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.max_pos = max_pos;
+  a.slots = slot_mapping;
+  a.k_top = k;
+  a.out = out_idx;
+  a.counters = static_cast<int32_t*>(workspace);
+  return hip_status(idx::launch_decode_step(a, static_cast<hipStream_t>(stream), num_cus()));
 }
 
 IDX_EXPORT int idx_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n, void* stream) {

@@ -30,6 +30,11 @@ struct KStoreArgs {
   const float* cos_sin;
   int32_t max_pos;
   const int64_t* slots;
+  // Decode-step rows (optional): row i = b*step_n_q + j is token
+  // clamp(ctx[b], 0, step_max_ctx) - step_n_q + j and is skipped when that is negative.
+  const int32_t* step_ctx = nullptr;
+  int32_t step_n_q = 0;
+  int32_t step_max_ctx = 0;
 };
 
 struct LogitsArgs {
@@ -64,6 +69,27 @@ bool logits_uses_decode_kernel(int n_q, int H);
 // into at most 256 chunks of at most 64 pages).
 int64_t logits_max_ctx(int n_q, int H, int page_size);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// The fused decode step: K store of the B*n_q new rows, scorer, top-k, in one launch.
+// Row i = b*n_q + j of k/positions/slots is token ctx[b] - n_q + j of sequence b.
+struct StepArgs {
+  LogitsArgs s;
+  const uint16_t* k;
+  int64_t row_stride;
+  const float* gamma;
+  double eps;
+  const int32_t* positions;
+  const float* cos_sin;
+  int32_t max_pos;
+  const int64_t* slots;
+  int32_t k_top;
+  int32_t* out;
+  int32_t* counters;  // [B] block counters: zero on entry, left zero on exit
+};
+// Whether the fused step takes this shape (n_q * ceil(H/16) <= 2 query head tiles per
+// sequence, rows of at most 16384 tokens).
+bool decode_step_supported(int n_q, int H, int64_t max_ctx);
+hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus);
 hipError_t launch_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n,
                             hipStream_t s);
 

@@ -1,0 +1,293 @@
+// Per-row top-k on gfx950, shared by the top-k kernel and the fused decode step (page
+// "Dense MXFP4 indexer for DeepSeek-V4 on ROCm", Purpose: 1024 tokens kept per query).
+//
+// One workgroup per row.  The row's valid cells are held in registers as order-
+// preserving 32-bit keys (thread t holds cells t, t+NT, t+2NT, ...: every load is a
+// contiguous 256-byte wave access, and all of a row's loads are in flight together).
+//   pass 1 — an LDS histogram of the top D1 key bits (13 for 1024-thread rows, 12 for
+//            smaller blocks, which share a CU several at a time) picks the digit d1
+//            holding the k-th key: cells above d1 are selected, cells below are not;
+//   one block scan of two per-thread counts (cells above the bucket, cells in it) gives
+//   every thread the output slots of its selected cells and the list slots of its
+//   bucket cells;
+//   the bucket (usually a few dozen keys) is resolved by ranking: each candidate counts
+//   the candidates ordered before it by (key desc, index asc); rank < the number still
+//   needed is selected, and the rank is its output slot.
+// A row whose bucket is larger than the ranking list (long runs of equal values) takes a
+// slower exact path: two more histogram passes over the register keys fix K*, and ranks
+// in index order come from wave ballots and per-(round, wave) counts.  Either way equal
+// logits resolve toward the smaller index and the output order is deterministic.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace idx {
+
+
+// Order-preserving key of a valid cell, never 0: -0.0 ranks equal to +0.0, and the one
+// pattern that would map to 0 (a negative NaN) shares key 1 with its neighbour.  Key 0
+// marks a cell past the row's valid length, so that cell ranks below every valid one.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k == 0u ? 1u : k;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
+
+constexpr int kRankCap = 1024;  // largest bucket resolved by ranking
+constexpr int kFbBins = 1024;   // histogram size of the two fallback passes
+
+template <int NT>
+struct Cfg {
+  static constexpr int D1 = NT >= 1024 ? 13 : 12;  // key bits resolved by pass 1
+  static constexpr int Shift = 32 - D1;
+  static constexpr int Bins = 1 << D1;
+  static constexpr int FbBitsA = 10;                // fallback pass A: next 10 bits
+  static constexpr int FbBitsB = Shift - FbBitsA;   // fallback pass B: the rest (9 or 10)
+};
+
+template <int NT, int EPT>
+struct alignas(16) TopkShared {
+  uint32_t hist[Cfg<NT>::Bins];
+  uint64_t cand[kRankCap];  // (key << 32) | ~index: one unsigned compare orders the bucket
+  int32_t wave_tot[2 * (NT / 64)];
+  int32_t cnt_gt[EPT * (NT / 64)];
+  int32_t cnt_eq[EPT * (NT / 64)];
+  int32_t sel_digit;
+  int32_t sel_above;
+};
+
+// Exclusive prefix sum of v over the block in thread order (and the block total): a DPP
+// wave scan, one LDS slot per wave, one barrier.  The caller keeps a barrier between two
+// calls (wave_tot is reused).
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = wave_tot[w];
+    tot += t;
+    if (w < wave) before += t;
+  }
+  total = tot;
+  return before + incl - v;
+}
+
+// Two exclusive prefix sums at once (one barrier): outputs the prefixes and the totals.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(int v0, int v1, int32_t* wave_tot, int& pre0, int& pre1, int& tot0,
+                                                 int& tot1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i0 = wave_incl_scan(v0), i1 = wave_incl_scan(v1);
+  if (lane == 63) {
+    wave_tot[2 * wave] = i0;
+    wave_tot[2 * wave + 1] = i1;
+  }
+  __syncthreads();
+  int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int x0 = wave_tot[2 * w], x1 = wave_tot[2 * w + 1];
+    t0 += x0;
+    t1 += x1;
+    if (w < wave) {
+      b0 += x0;
+      b1 += x1;
+    }
+  }
+  pre0 = b0 + i0 - v0;
+  pre1 = b1 + i1 - v1;
+  tot0 = t0;
+  tot1 = t1;
+}
+
+// Given a histogram of BINS digits (BINS >= NT), find the digit d holding the kk-th
+// largest item (kk >= 1): count(digits > d) < kk <= count(digits >= d).  Thread t covers
+// BINS/NT digits, the highest to thread 0; only the thread whose range holds the answer
+// re-reads its bins.  Leaves d and count(> d) in shared memory (two barriers).
+template <int NT, int BINS, class SH>
+__device__ __forceinline__ void select_digit(SH& sh, int kk) {
+  constexpr int PER = BINS / NT;
+  const int hi = BINS - PER * (int)threadIdx.x;  // digits [hi - PER, hi)
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) local += (int)sh.hist[hi - 1 - q];
+  int total;
+  int before = block_excl_scan<NT>(local, sh.wave_tot, total);
+  if (before < kk && kk <= before + local) {
+    for (int q = 0; q < PER; ++q) {
+      const int c = (int)sh.hist[hi - 1 - q];
+      if (before < kk && kk <= before + c) {
+        sh.sel_digit = hi - 1 - q;
+        sh.sel_above = before;
+      }
+      before += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Top-k of one row by one workgroup of NT threads: `row` holds n valid cells (n <= NT*EPT),
+// the k selected indices (or 0..n-1 then -1 when n <= k) go to out[0..k).  Every thread
+// of the block calls it with the same arguments.
+template <int NT, int EPT>
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
+                                         TopkShared<NT, EPT>& sh) {
+  using C = Cfg<NT>;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n <= k) {
+    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  const int ne = (n + NT - 1) / NT;  // rounds that hold valid cells (uniform)
+  // Branch-free loads at an in-bounds index (cells past n read cell n-1 and are masked),
+  // so all loads are in flight together; the histogram is cleared while they are.
+  float raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) raw[e] = row[min(e * NT + tid, n - 1)];
+  for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
+  uint32_t key[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) key[e] = (e * NT + tid < n) ? float_key(raw[e]) : 0u;
+  __syncthreads();
+
+  // ---- pass 1: the top D1 bits of every valid cell ----
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (e < ne && key[e] != 0u) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
+  __syncthreads();
+  select_digit<NT, C::Bins>(sh, k);
+  const uint32_t d1 = (uint32_t)sh.sel_digit;
+  int kk = k - sh.sel_above;
+
+  // ---- cells above the bucket, and the bucket itself (one block scan of two counts) ----
+  // Cells past n (key 0) can only fall in the bucket when d1 == 0; they then rank below
+  // every valid candidate, and the histogram (valid cells only) needs fewer than those.
+  int n_gt = 0, n_in = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t dg = key[e] >> C::Shift;
+    n_gt += dg > d1 ? 1 : 0;
+    n_in += dg == d1 ? 1 : 0;
+  }
+  int tot_gt, nc, pos_gt, pos_in;
+  block_excl_scan2<NT>(n_gt, n_in, sh.wave_tot, pos_gt, pos_in, tot_gt, nc);
+  if (nc <= kRankCap) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if ((key[e] >> C::Shift) == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
+    __syncthreads();
+    // Rank of each candidate among the bucket by (key desc, index asc); composites are
+    // distinct, so the ranks are a permutation of 0..nc-1.  G adjacent lanes share one
+    // candidate (G = NT / nc rounded to a power of two, at most 64), each counting a
+    // strided part of the list, and a lane-xor reduction sums their counts.
+    int np2 = 1;
+    while (np2 < nc) np2 <<= 1;
+    const int G = max(1, min(64, NT / np2));
+    const int per_sweep = NT / G;
+    for (int base = 0; base < nc; base += per_sweep) {
+      const int c = base + tid / G, part = tid & (G - 1);
+      const uint64_t me = sh.cand[min(c, nc - 1)];
+      int cnt = 0;
+      if (c < nc) {
+        int t = part;
+        for (; t + 7 * G < nc; t += 8 * G) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cnt += sh.cand[t + u * G] > me ? 1 : 0;
+        }
+        for (; t < nc; t += G) cnt += sh.cand[t] > me ? 1 : 0;
+      }
+      for (int m = 1; m < G; m <<= 1) cnt += shfl_xor(cnt, m);
+      if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = (int32_t)~(uint32_t)me;
+    }
+    // cells above the bucket: after the barriers, so no store is waited for
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = e * NT + tid;
+    return;
+  }
+
+  // ---- large bucket: fallback passes A and B over the register keys fix K* ----
+  uint32_t prefix = d1 << C::Shift, pmask = ~0u << C::Shift;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? C::Shift - C::FbBitsA : 0;
+    const uint32_t dmask = pass == 0 ? (1u << C::FbBitsA) - 1u : (1u << C::FbBitsB) - 1u;
+    for (int i = tid; i < kFbBins; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (e < ne && key[e] != 0u && (key[e] & pmask) == prefix)
+        atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1u);
+    __syncthreads();
+    select_digit<NT, kFbBins>(sh, kk);
+    prefix |= (uint32_t)sh.sel_digit << shift;
+    pmask |= dmask << shift;
+    kk -= sh.sel_above;
+    __syncthreads();
+  }
+  const uint32_t kstar = prefix;
+  const int need_eq = kk;  // how many cells equal to K* are taken (>= 1)
+
+  // ---- ranks in index order: per (round e, wave) counts of >K* and ==K* cells ----
+  // Cell i = e*NT + wave*64 + lane, so (e, wave) pairs in row-major order are index order.
+  constexpr int NE = EPT * NW;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {  // kstar >= 1, so cells past n (key 0) never count
+    const uint64_t bg = __ballot(key[e] > kstar);
+    const uint64_t be = __ballot(key[e] == kstar);
+    if (lane == 0) {
+      sh.cnt_gt[e * NW + wave] = __popcll(bg);
+      sh.cnt_eq[e * NW + wave] = __popcll(be);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scan of both count arrays by one wave
+    constexpr int PER = (NE + 63) / 64;
+    int g[PER], q[PER], sg = 0, se = 0;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int f = lane * PER + t;
+      g[t] = f < NE ? sh.cnt_gt[f] : 0;
+      q[t] = f < NE ? sh.cnt_eq[f] : 0;
+      sg += g[t];
+      se += q[t];
+    }
+    int ig = wave_incl_scan(sg) - sg, ie = wave_incl_scan(se) - se;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int f = lane * PER + t;
+      if (f < NE) {
+        sh.cnt_gt[f] = ig;
+        sh.cnt_eq[f] = ie;
+      }
+      ig += g[t];
+      ie += q[t];
+    }
+  }
+  __syncthreads();
+  const uint64_t lt = lanemask_lt(lane);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (e < ne) {
+      const int i = e * NT + tid;
+      const bool is_gt = key[e] > kstar;
+      const bool is_eq = key[e] == kstar;
+      const uint64_t bg = __ballot(is_gt);
+      const uint64_t be = __ballot(is_eq);
+      const int gt_before = sh.cnt_gt[e * NW + wave] + __popcll(bg & lt);
+      const int eq_before = sh.cnt_eq[e * NW + wave] + __popcll(be & lt);
+      const int pos = gt_before + min(eq_before, need_eq);
+      if ((is_gt || (is_eq && eq_before < need_eq)) && pos < k) out[pos] = i;
+    }
+  }
+}
+
+}  // namespace idx

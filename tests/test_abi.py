@@ -129,6 +129,37 @@ def test_topk_checks(lib):
     assert f(FAKE, 1 << 20, FAKE, 2, 1, 65537, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
 
 
+def step_call(lib, p=None, **kw):
+    """idx_decode_step with valid-looking fake pointers (decode B2/H32/ctx256, k 64)."""
+    P = p if p is not None else pool()
+    d = dict(k=FAKE, rs=128, g=FAKE, eps=1e-6, pos=FAKE, cs=FAKE, mp=512, sl=FAKE, q=FAKE, qs=FAKE, w=FAKE, pt=FAKE,
+             mpp=4, ctx=FAKE, B=2, n_q=1, H=32, D=128, mc=256, lg=FAKE, ls=256, kk=64, out=FAKE, ws=FAKE,
+             wsb=lib.idx_decode_step_workspace_bytes(2))
+    d.update(kw)
+    return lib.idx_decode_step(ctypes.byref(P), d["k"], d["rs"], d["g"], ctypes.c_float(d["eps"]), d["pos"], d["cs"],
+                               d["mp"], d["sl"], d["q"], d["qs"], d["w"], d["pt"], d["mpp"], d["ctx"], d["B"],
+                               d["n_q"], d["H"], d["D"], d["mc"], d["lg"], ctypes.c_int64(d["ls"]), d["kk"], d["out"],
+                               d["ws"], ctypes.c_size_t(d["wsb"]), None)
+
+
+def test_decode_step_checks(lib):
+    assert lib.idx_decode_step_workspace_bytes(0) == 0
+    assert lib.idx_decode_step_workspace_bytes(1) == 256 and lib.idx_decode_step_workspace_bytes(65) == 512
+    assert step_call(lib, ws=None) == bd.IDX_EINVAL
+    assert step_call(lib, wsb=0) == bd.IDX_EINVAL
+    assert step_call(lib, ws=FAKE + 2) == bd.IDX_EALIGN
+    assert step_call(lib, sl=None) == bd.IDX_EINVAL
+    assert step_call(lib, rs=64) == bd.IDX_EINVAL
+    assert step_call(lib, kk=0) == bd.IDX_EINVAL
+    assert step_call(lib, D=64) == bd.IDX_EUNSUPPORTED
+    assert step_call(lib, H=48) == bd.IDX_EUNSUPPORTED                   # 3 head tiles
+    assert step_call(lib, n_q=2, wsb=lib.idx_decode_step_workspace_bytes(2)) == bd.IDX_EUNSUPPORTED  # 4 tiles
+    assert step_call(lib, mc=16385, mpp=1 << 10, ls=1 << 15) == bd.IDX_EUNSUPPORTED
+    assert step_call(lib, mc=257) == bd.IDX_EINVAL                       # beyond the page table
+    if no_gpu(lib):
+        assert step_call(lib) == bd.IDX_EUNSUPPORTED
+
+
 def test_quant_checks(lib):
     assert lib.idx_q_quant_mxfp4(FAKE, -1, FAKE, FAKE, None) == bd.IDX_EINVAL
     assert lib.idx_q_quant_mxfp4(None, 4, FAKE, FAKE, None) == bd.IDX_EINVAL
