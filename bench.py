@@ -118,11 +118,18 @@ def traffic_from_profiles(kernel_key, src_hash):
     return None
 
 
-SCORER_SOURCES = ("logits.hip", "device_common.hpp", "launch.hpp")
+SCORER_SOURCES = ("logits.hip", "scorer.hpp", "device_common.hpp", "launch.hpp")
 
 
 def scorer_source_hash():
     return source_hash([os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in SCORER_SOURCES])
+
+
+FUSED_SOURCES = SCORER_SOURCES + ("decode_step.hip", "topk_row.hpp", "kstore_row.hpp")
+
+
+def fused_source_hash():
+    return source_hash([os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in FUSED_SOURCES])
 
 
 def _short_kernel(name):
@@ -185,22 +192,27 @@ def summarize(dirs, traffic_key=None, calib_mib=0):
     scorer = lambda k: k.startswith("logits_")
     copy = lambda k: "copyBuffer" in k
     big = lambda vals: max(vals, key=lambda t: t[2])  # the largest grid = the timed launches
-    _, fetch, _ = pick(scorer, "FETCH_SIZE", big)
-    _, write, _ = pick(scorer, "WRITE_SIZE", big)
     known_kib = calib_mib * 1024.0
     f_fetch = known_kib / pick(copy, "FETCH_SIZE", lambda v: max(t[2] for t in v))
     f_write = known_kib / pick(copy, "WRITE_SIZE", lambda v: max(t[2] for t in v))
-    entry = {"fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
-             "copy_scale_fetch": round(f_fetch, 4), "copy_scale_write": round(f_write, 4),
-             "hbm_bytes_per_launch": int(round((fetch * f_fetch + write * f_write) * 1024)),
-             "source_hash": scorer_source_hash()}
     p = os.path.join(ROOT, "profiles", "traffic.json")
     d = json.load(open(p)) if os.path.exists(p) else {}
-    d[traffic_key] = entry
+    fused = lambda k: k.startswith("decode_step_kernel")
+    for key, pred, shash in ((traffic_key, scorer, scorer_source_hash()),
+                             (traffic_key + "_fused", fused, fused_source_hash())):
+        if not any(pred(k) and c == "FETCH_SIZE" for (k, g, c) in counters):
+            continue
+        _, fetch, _ = pick(pred, "FETCH_SIZE", big)
+        _, write, _ = pick(pred, "WRITE_SIZE", big)
+        entry = {"fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+                 "copy_scale_fetch": round(f_fetch, 4), "copy_scale_write": round(f_write, 4),
+                 "hbm_bytes_per_launch": int(round((fetch * f_fetch + write * f_write) * 1024)),
+                 "source_hash": shash}
+        d[key] = entry
+        print(f"\n{key}: {json.dumps(entry)}")
     with open(p, "w") as fh:
         json.dump(d, fh, indent=1, sort_keys=True)
         fh.write("\n")
-    print(f"\n{traffic_key}: {json.dumps(entry)}")
 
 
 def cpu_baseline(W, fmt, budget_s):
@@ -485,6 +497,14 @@ def main():
                          "score_plus_topk": round(s_mean + t_mean, 3),
                          "note": "each kernel alone, back to back; per-call mean (p10/p90 over groups of 10 calls)"},
         "roofline": roof,
+        "fused_roofline": None if fused_us is None else {
+            "bound": "hbm", "kernel": "decode_step_kernel",
+            "algorithmic_bytes": ab["scorer"] + ab["topk"] + ab["kstore"],
+            "achieved": round((ab["scorer"] + ab["topk"] + ab["kstore"]) / (fused_us * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round((ab["scorer"] + ab["topk"] + ab["kstore"]) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(f"cfg{args.config}_{args.kv}_fused", fused_source_hash()),
+            "note": "the whole step in one launch (K store + scorer + top-k); latency of the top-k tail included"},
         "topk_hbm_gbs": round(ab["topk"] / (t_mean * 1e-6) / 1e9, 1),
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }
