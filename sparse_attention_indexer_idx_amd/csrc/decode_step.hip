@@ -4,10 +4,11 @@
 // decode sizes each of them is mostly launch and dependency latency, so here they share one.
 //
 // Blocks of 16 waves; each wave scores 128 consecutive tokens of one sequence with the
-// decode-form wave body (scorer.hpp).  In a block whose range holds new tokens, wave 0
-// first computes their K rows (kstore_row.hpp) and stores them to their slots for later
-// steps; after one barrier the wave holding a new token substitutes the fresh bytes into
-// its K tile in registers, so no wave reads a row back from the pool it is written to.  Each
+// decode-form wave body (scorer.hpp).  For each of the step's new tokens in a block, the
+// wave holding the token leaves its logit out, and wave 0 — after its own scoring —
+// computes the token's K row (kstore_row.hpp), stores it to its slot for later steps and
+// scores the token from the fresh row in registers; nothing reads a row back from the
+// pool it is written to, and no wave waits for the K store.  Each
 // block then publishes its logits (device-coherent stores) and counts itself in on the
 // sequence's counter; the last block of a sequence invalidates its caches once and runs
 // the top-k of the sequence's rows with all 1024 threads (topk_row.hpp), then resets the
@@ -24,93 +25,87 @@ constexpr int kStepG = 2;       // 128 tokens per wave
 constexpr int kStepTok = kStepWaves * 64 * kStepG;
 constexpr int kStepMaxTiles = 2;  // query head tiles per sequence (register budget of 1024-thread blocks)
 constexpr int kStepMaxCtx = 16 * 1024;
-constexpr int kRowWords = 34;   // one K row in page layout (16 or 32 data words, scale word) + flag
+constexpr int kRowWords = 33;   // one K row in page layout: 16 (or 32) data words, then the scale word
 
-// The block's new K rows.  pre(): wave 0 of a block whose token range holds new tokens
-// computes those rows (before its own loads, so the fp64 work never shares registers with
-// K tiles in flight), stores them to their slots and leaves their bytes in LDS.
-// operator(): after every wave has issued its K loads, one barrier, then the wave holding
-// a new token substitutes the row into its tile in registers.
+// The step's new K rows.  prepare(): every wave of the block learns which of the newest
+// n_q tokens fall in the block and have a row to store (valid slot and position); the
+// wave holding such a token skips its logit.  Wave 0 — the first to have its K bytes, so
+// the first to finish scoring — then computes each such row after its own work (its K
+// tiles are no longer live, so the fp64 work has registers to spare), stores it to its
+// slot, leaves it in its LDS buffer, and rescores the token from it.
 template <int FMT>
 struct NewRows {
   static constexpr bool kCoherentStores = true;
+  static constexpr bool kNewRows = true;
   const StepArgs* a;
   int b;
   int blk0;        // first token of the block
-  int n_b;         // the sequence's length (clamped to max_ctx)
-  bool any;        // block-uniform: the block holds a new token
-  uint32_t (*buf)[kRowWords];  // [n_q] LDS rows; words[kRowWords - 1] = 1 when row j was stored
+  bool wave0;
+  uint32_t* buf;   // wave 0's LDS row buffer (kRowWords words)
+  int s_new[kStepMaxTiles];  // new tokens of the block with a row to store, else -1
 
-  __device__ __forceinline__ bool holds(int s) const { return s >= blk0 && s < blk0 + kStepTok; }
-
-  __device__ __forceinline__ void pre(int lane) const {
-    if (!any || (threadIdx.x >> 6) != 0) return;
+  __device__ __forceinline__ void prepare(int n_b) {
     const int n_q = a->s.n_q;
-    const int64_t P = a->s.pool.page_size;
-    for (int j = 0; j < n_q; ++j) {  // uniform
-      const int s = n_b - n_q + j;
-      bool stored = false;
-      if (s >= 0 && holds(s)) {
-        const int64_t i = (int64_t)b * n_q + j;
-        const int64_t slot = a->slots[i];
-        const int32_t pos = a->positions[i];
-        if (slot >= 0 && slot < a->s.pool.num_pages * P && pos >= 0 && pos < a->max_pos) {
-          kstore_row<FMT>(a->s.pool, a->k + i * a->row_stride, a->gamma, a->eps, a->cos_sin + (int64_t)pos * 64,
-                          slot, lane, buf[j]);
-          stored = true;
-        }
-      }
-      if (lane == 0) buf[j][kRowWords - 1] = stored ? 1u : 0u;
+#pragma unroll
+    for (int jn = 0; jn < kStepMaxTiles; ++jn) {
+      s_new[jn] = -1;
+      if (jn >= n_q) continue;
+      const int s = n_b - n_q + jn;
+      if (s < 0 || s < blk0 || s >= blk0 + kStepTok) continue;
+      const int64_t i = (int64_t)b * n_q + jn;
+      const int64_t slot = a->slots[i];
+      const int32_t pos = a->positions[i];
+      if (slot < 0 || slot >= a->s.pool.num_pages * (int64_t)a->s.pool.page_size || pos < 0 || pos >= a->max_pos)
+        continue;
+      s_new[jn] = s;
     }
   }
 
-  template <class KT>
-  __device__ __forceinline__ void operator()(KT& kt, int tok0, int, int lane) const {
-    if (!any) return;
-    __syncthreads();  // the rows in LDS are complete
-    constexpr int T = sizeof(KT) / sizeof(kt[0]);
-    const int n_q = a->s.n_q;
-    for (int j = 0; j < n_q; ++j) {  // uniform
-      const int s = n_b - n_q + j;
-      if (s < tok0 || s >= tok0 + 16 * T || buf[j][kRowWords - 1] == 0u) continue;
-      const uint32_t* w = buf[j];
-      const int tt = (s - tok0) >> 4, g = lane >> 4;
-      const bool mine = (lane & 15) == (s & 15);
-      v8i v;
-      uint32_t sc;
-      if (FMT == 0) {
-        v = v8i{(int)w[4 * g], (int)w[4 * g + 1], (int)w[4 * g + 2], (int)w[4 * g + 3], 0, 0, 0, 0};
-        sc = (w[16] >> (8 * g)) & 0xFFu;
-      } else {
+  __device__ __forceinline__ bool skip(int s) const {
+    bool k = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (int)w[8 * g + e];
-        sc = w[32];
-      }
+    for (int jn = 0; jn < kStepMaxTiles; ++jn) k = k || s == s_new[jn];
+    return k;
+  }
+
+  __device__ __forceinline__ bool rescorer() const { return wave0; }
+
+  template <int F>
+  __device__ __forceinline__ bool new_row(int jn, int lane, KTile<F>& nk, int& s, int& slot4) const {
+    if (jn >= kStepMaxTiles || s_new[jn] < 0) return false;
+    s = s_new[jn];
+    const int64_t i = (int64_t)b * a->s.n_q + jn;
+    const int32_t pos = a->positions[i];
+    kstore_row<F>(a->s.pool, a->k + i * a->row_stride, a->gamma, a->eps, a->cos_sin + (int64_t)pos * 64,
+                  a->slots[i], lane, buf);
+    __builtin_amdgcn_wave_barrier();  // the row words are written by a few lanes, read by all
+    const int g = lane >> 4;
+    if (F == 0) {
+      nk.v = v8i{(int)buf[4 * g], (int)buf[4 * g + 1], (int)buf[4 * g + 2], (int)buf[4 * g + 3], 0, 0, 0, 0};
+      nk.scale = (buf[16] >> (8 * g)) & 0xFFu;
+    } else {
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const bool hit = mine && t == tt;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kt[t].v[e] = hit ? v[e] : kt[t].v[e];
-        kt[t].scale = hit ? sc : kt[t].scale;
-      }
+      for (int e = 0; e < 8; ++e) nk.v[e] = (int)buf[8 * g + e];
+      nk.scale = buf[32];
     }
+    __builtin_amdgcn_wave_barrier();  // the buffer is reused by the next new row
+    slot4 = ((s - blk0) >> 4) & 3;    // the token's tile slot within its own wave's group
+    return true;
   }
 };
 
 template <int FMT, int NT, int EPT>
 __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
   __shared__ TopkShared<1024, EPT> sh;
-  __shared__ uint32_t rows[kStepMaxTiles][kRowWords];
+  __shared__ uint32_t row_buf[kRowWords];
   __shared__ int last;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int b = blockIdx.y;
   const int blk0 = blockIdx.x * kStepTok;
   const int tok0 = blk0 + wave * (64 * kStepG);
-  const int n_b = uniform(min(max(a.s.ctx[b], 0), a.s.max_ctx));
-  // block-uniform: the newest n_q tokens [n_b - n_q, n_b) meet [blk0, blk0 + kStepTok)
-  const bool any = n_b > blk0 && n_b - a.s.n_q < blk0 + kStepTok;
-  decode_wave<FMT, NT, kStepG>(a.s, b, tok0, lane, NewRows<FMT>{&a, b, blk0, n_b, any, rows});
+  NewRows<FMT> nr{&a, b, blk0, wave == 0, row_buf, {}};
+  decode_wave<FMT, NT, kStepG>(a.s, b, tok0, lane, nr);
 
   // Publish this block's logits and count it in.  The logits stores are device-coherent
   // (they write through to the level every XCD reads), and every wave waits until its
@@ -127,6 +122,7 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
   }
   __syncthreads();
   if (!last) return;
+  const int n_b = min(max(a.s.ctx[b], 0), a.s.max_ctx);
   for (int j = 0; j < a.s.n_q; ++j) {
     const int64_t r = (int64_t)b * a.s.n_q + j;
     topk_row<1024, EPT>(a.s.logits + r * a.s.lstride, valid_len(n_b, a.s.n_q, j), a.k_top, a.out + r * a.k_top, sh);

@@ -35,7 +35,8 @@ template <int FMT, int NT, int G>
 __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const int tok0 = (blockIdx.x * kDecodeWaves + wave) * (64 * G);
-  decode_wave<FMT, NT, G>(a, blockIdx.y, tok0, threadIdx.x & 63, NoPatch{});
+  NoPatch none;
+  decode_wave<FMT, NT, G>(a, blockIdx.y, tok0, threadIdx.x & 63, none);
 }
 
 // ------------------------------------------------------------------------------------

@@ -133,24 +133,28 @@ __device__ __forceinline__ float relu_dot(const v4f& d, const v4f& w) {
 // Decode: every query row of a sequence in registers (n_q * ceil(H/16) <= 16 head
 // tiles), one wave per G*64 consecutive cached tokens (G groups of four 16-token tiles).
 // Per wave: Q and w loads, then the page ids of its tiles and the sequence length
-// together, then all K loads, before the first use.  `patch.pre(lane)` runs first and
-// `patch(kt, tok0, n_b, lane)` may rewrite K tiles in registers after their loads are
-// issued (both no-ops for the plain scorer); Patch::kCoherentStores makes the logits
-// stores device-coherent.
+// together, then all K loads, before the first use.  Patch::kCoherentStores makes the
+// logits stores device-coherent; Patch::kNewRows rescores new tokens at the end.
 // ------------------------------------------------------------------------------------
 constexpr int kDecodeMaxTiles = 16;
 
+// Hooks of the decode wave body: the plain scorer has none; the fused decode step stores
+// its logits device-coherently and rescoring its new tokens (see NewRows).
 struct NoPatch {
   static constexpr bool kCoherentStores = false;
-  __device__ __forceinline__ void pre(int) const {}
-  template <class KT>
-  __device__ __forceinline__ void operator()(KT&, int, int, int) const {}
+  static constexpr bool kNewRows = false;
+  __device__ __forceinline__ void prepare(int) {}
+  __device__ __forceinline__ bool skip(int) const { return false; }
+  __device__ __forceinline__ bool rescorer() const { return false; }
+  template <int FMT>
+  __device__ __forceinline__ bool new_row(int, int, KTile<FMT>&, int&, int&) const {
+    return false;
+  }
 };
 
 template <int FMT, int NT, int G, class Patch>
-__device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, const Patch& patch) {
+__device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, Patch& patch) {
   constexpr int T = 4 * G;  // K tiles per wave
-  patch.pre(lane);
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int last_page = (a.max_ctx - 1) >> lgP;
   const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
@@ -178,6 +182,7 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
   for (int t = 0; t < T; ++t) pid[t] = uniform(ptb[std::min((tok0 + 16 * t) >> lgP, last_page)]);
   const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
   const bool live = tok0 < n_b;  // n_b <= max_ctx, so this also covers waves past max_ctx
+  patch.prepare(n_b);
 
   // K tiles: a tile of a dead wave or on an invalid page reads page 0 row 0 (always
   // inside the pool); invalid pages score NaN below, dead waves store nothing.
@@ -192,40 +197,69 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
     kt[t] = load_k_tile<FMT, true>(page, P, use ? (s0 & (P - 1)) : 0, lane);
     ok[t] = valid_page;  // tiles past n_b are computed but never stored
   }
-  patch(kt, tok0, n_b, lane);  // the fused decode step's new K rows (no-op otherwise)
 
   const float qnan = __builtin_nanf("");
-  // Head tiles m = j*HT .. j*HT+HT-1 belong to query row j.  Every MFMA runs
-  // unconditionally (so nothing sinks the Q loads behind a branch); a row is finished —
-  // head reduction, transpose, store — once its last tile is in.  A dead wave (tok0 >= n_b)
-  // stores nothing: s >= tok0 >= n_b >= every valid length.
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int s = tok0 + 64 * g + lane;
+  auto store = [&](int j, int s, float logit) {
+    float* dst = a.logits + ((int64_t)b * a.n_q + j) * a.lstride + s;
+    if (Patch::kCoherentStores)  // device-coherent: visible to other XCDs once complete
+      __hip_atomic_store(dst, logit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *dst = logit;
+  };
+  // One group of four 16-token tiles: head tiles m = j*HT .. j*HT+HT-1 belong to query
+  // row j; every MFMA runs unconditionally (so nothing sinks the Q loads behind a branch),
+  // and a row is finished — head reduction, transpose, emit — once its last tile is in.
+  // Lane l of the result holds token s0 + l.
+  auto score_group = [&](const KTile<FMT>* k4, const bool* ok4, auto&& emit) {
     float acc[4];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float v = relu_dot(mfma<FMT>(qa[m], qs[m], kt[4 * g + t]), qw[m]);
+        const float v = relu_dot(mfma<FMT>(qa[m], qs[m], k4[t]), qw[m]);
         acc[t] = (m % HT == 0) ? v : acc[t] + v;
       }
       if ((m + 1) % HT == 0) {  // uniform
-        const int j = m / HT;
         float p[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float v = FMT == 1 ? acc[t] * __uint_as_float(kt[4 * g + t].scale) : acc[t];
-          p[t] = ok[4 * g + t] ? v : qnan;
+          const float v = FMT == 1 ? acc[t] * __uint_as_float(k4[t].scale) : acc[t];
+          p[t] = ok4[t] ? v : qnan;
         }
-        const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
-        if (s < valid_len(n_b, a.n_q, j)) {
-          float* dst = a.logits + ((int64_t)b * a.n_q + j) * a.lstride + s;
-          if (Patch::kCoherentStores)  // device-coherent: visible to other XCDs once complete
-            __hip_atomic_store(dst, logit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          else
-            *dst = logit;
-        }
+        emit(m / HT, reduce4_transpose(p[0], p[1], p[2], p[3]));
+      }
+    }
+  };
+  // A dead wave (tok0 >= n_b) stores nothing: s >= tok0 >= n_b >= every valid length.
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int s = tok0 + 64 * g + lane;
+    score_group(&kt[4 * g], &ok[4 * g], [&](int j, float logit) {
+      if (s < valid_len(n_b, a.n_q, j) && !patch.skip(s)) store(j, s, logit);
+    });
+  }
+
+  if constexpr (Patch::kNewRows) {
+    // The fused decode step's new tokens: the wave that holds one skips its logit above,
+    // and one early-finishing wave of the block computes the token's K row (stored to
+    // the pool for later steps) and scores the token from the fresh row, in the tile slot
+    // and lane the token occupies in its own wave, so the logit is bit-identical to
+    // scoring a pool that already held the row.  Only column (token % 16) of the new
+    // tile matters.
+    if (patch.rescorer()) {
+      for (int jn = 0; jn < a.n_q; ++jn) {  // uniform
+        KTile<FMT> nk;
+        int s_new, slot4;
+        if (!patch.template new_row<FMT>(jn, lane, nk, s_new, slot4)) continue;
+        // page validity of the token's tile, as its own wave sees it
+        const int32_t pid_new = uniform(ptb[std::min(s_new >> lgP, last_page)]);
+        const bool okt = pid_new >= 0 && (int64_t)pid_new < a.pool.num_pages;
+        const KTile<FMT> k4[4] = {nk, nk, nk, nk};
+        const bool ok4[4] = {okt, okt, okt, okt};
+        const bool mine = lane == 16 * slot4 + (s_new & 15);
+        score_group(k4, ok4, [&](int j, float logit) {
+          if (mine && s_new < valid_len(n_b, a.n_q, j)) store(j, s_new, logit);
+        });
       }
     }
   }
