@@ -393,6 +393,16 @@ def main():
     k_mean, k_us = held(k_store, args.steps, host_s)
     s_mean, s_us = held(score, args.steps, host_s)
     t_mean, t_us = held(topk, args.steps, host_s)
+    qprep_us = None
+    if fmt == 0:
+        # The Q-side preparation that feeds the scorer (rotation + MXFP4 packing + weight
+        # fold of every query row's heads), timed alone; it is not part of the step.
+        q3 = q_bf16.view(W.rows, W.H, 128)
+        qpos = dev(np.array([max(W.valid_len(r) - 1, 0) for r in range(W.rows)], np.int32))
+        qp2, qs2 = torch.empty_like(q), torch.empty_like(qs)
+        w2 = torch.empty_like(w)
+        qprep_us, _ = held(lambda i: bd.idx_q_prep_mxfp4(q3, qpos, cos_sin, w, 0.0625, qp2, qs2, w2), args.steps,
+                           host_s)
 
     # The step captured into HIP graphs, as a serving loop runs the indexer inside a
     # captured forward pass: graph A holds L consecutive steps (L a multiple of the replica
@@ -505,6 +515,7 @@ def main():
             "frac": round((ab["scorer"] + ab["topk"] + ab["kstore"]) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profiles(f"cfg{args.config}_{args.kv}_fused", fused_source_hash()),
             "note": "the whole step in one launch (K store + scorer + top-k); latency of the top-k tail included"},
+        "q_prep_us": None if qprep_us is None else round(qprep_us, 3),
         "topk_hbm_gbs": round(ab["topk"] / (t_mean * 1e-6) / 1e9, 1),
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }

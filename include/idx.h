@@ -129,6 +129,32 @@ int idx_k_store_fp8(const idx_pool* pool, const void* k_bf16, int64_t n_rows, in
  * ------------------------------------------------------------------------------- */
 int idx_q_quant_mxfp4(const void* q_bf16, int64_t n_vecs, uint8_t* q_packed, uint8_t* q_scale, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * MXFP4 Q preparation for the scorer: rotation, packing and the weight fold in one op.
+ * Page "Dense MXFP4 indexer for DeepSeek-V4 on ROCm", Changes / Q quant: the Q op rotates
+ * and packs Q to MXFP4 and emits fp32 weights with the softmax and head scales folded in;
+ * page "[ROCm][Perf] Fuse DSA indexer QK preprocessing with AITER", Purpose: RoPE covers
+ * the leading rope dims of q as of k.
+ *
+ * Vector v = t * H + h is head h of token t.  Its leading 64 dims are rotated at
+ * positions[t] with the K store's NeoX rotation (pairs (i, i+32), fp64, no fused
+ * operations, the same cos_sin table), dims 64..127 pass through, and the result is
+ * packed exactly as idx_q_quant_mxfp4 packs a vector (bit-exact against a CPU
+ * implementation).  A position outside [0, max_pos) leaves its token's vectors
+ * unrotated.  w_out[v] = fp32(w[v] * w_scale), where w_scale is the product of the
+ * factors folded in (for example head_dim^-1/2 * H^-1/2).
+ *
+ * q_bf16     device bf16 [n_tokens][H][128];  positions device int32 [n_tokens];
+ * cos_sin    device fp32 [max_pos][64] (32 cosines, 32 sines per position);
+ * w          device fp32 [n_tokens][H];  w_out device fp32 [n_tokens][H];
+ * q_packed   device uint8 [n_tokens][H][64], 4-byte aligned;
+ * q_scale    device uint8 [n_tokens][H][4], 4-byte aligned.
+ * n_tokens >= 0 (0 is a no-op); H in [1, 128].
+ * ------------------------------------------------------------------------------- */
+int idx_q_prep_mxfp4(const void* q_bf16, int64_t n_tokens, int32_t H, const int32_t* positions, const float* cos_sin,
+                     int32_t max_pos, const float* w, float w_scale, uint8_t* q_packed, uint8_t* q_scale, float* w_out,
+                     void* stream);
+
 /* FP8 Q with one scale per 128-dim head vector, multiplied into that head's weight
  * (page "[ROCm][Perf] Fuse DSA indexer QK preprocessing with AITER", Purpose: q is FP8
  * quantised per token group and its scale is then folded into the indexer weights):

@@ -2,7 +2,8 @@
 
 A plain fp64 CPU implementation (``idx_oracle.c``) of what the hot path computes:
 the MXFP4 / FP8 codecs, the K-cache store (RMSNorm -> NeoX RoPE -> quantise -> page
-store), the paged MQA logits with the causal/length mask, and the per-row top-k.
+store), the Q packing and the MXFP4 Q preparation (NeoX RoPE -> pack -> weight fold),
+the paged MQA logits with the causal/length mask, and the per-row top-k.
 Each C function cites the page passage it follows.
 
 Only the test suite, the package smoke check and the benchmark's CPU-baseline leg may
@@ -62,6 +63,7 @@ def _load():
                 "orc_k_rows_exact": (None, [P, I64, I64, P, F32, P, P, P]),
                 "orc_q_quant_mxfp4": (None, [P, I64, P, P]),
                 "orc_q_quant_fp8": (None, [P, P, I64, P, P]),
+                "orc_q_prep_mxfp4": (None, [P, I64, I32, P, P, I32, P, F32, P, P, P]),
                 "orc_valid_len": (I64, [P, I32, I64]),
                 "orc_logits_paged": (ctypes.c_int, [P, I64, I64, I64, I32, I32, P, P, P, P, I32, P, I32, I32, I32,
                                                     P, I64, P, I64]),
@@ -154,6 +156,23 @@ def q_quant_mxfp4(q_bf16: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     qs = np.empty(q.shape[:-1] + (4,), np.uint8)
     _load().orc_q_quant_mxfp4(_p(q), n, _p(qp), _p(qs))
     return qp, qs
+
+
+def q_prep_mxfp4(q_bf16: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray, w: np.ndarray,
+                 w_scale: float) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """q_bf16 [T, H, 128] uint16, positions [T], w [T, H] -> (packed [T, H, 64] uint8,
+    scales [T, H, 4] uint8, w_out [T, H] fp32): rotation, MXFP4 packing, weight fold."""
+    q_bf16 = np.ascontiguousarray(q_bf16, np.uint16)
+    T, H = q_bf16.shape[0], q_bf16.shape[1]
+    assert q_bf16.shape[2] == 128
+    cos_sin = np.ascontiguousarray(cos_sin, np.float32)
+    out = np.empty((T, H, 64), np.uint8)
+    sc = np.empty((T, H, 4), np.uint8)
+    wo = np.empty((T, H), np.float32)
+    _load().orc_q_prep_mxfp4(_p(q_bf16), T, H, _p(np.ascontiguousarray(positions, np.int32)), _p(cos_sin),
+                             cos_sin.shape[0], _p(np.ascontiguousarray(w, np.float32)), w_scale, _p(out), _p(sc),
+                             _p(wo))
+    return out, sc, wo
 
 
 def q_quant_fp8(q_bf16: np.ndarray, w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

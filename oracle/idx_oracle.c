@@ -272,6 +272,44 @@ void orc_q_quant_mxfp4(const uint16_t* q_bf16, int64_t n_vecs, uint8_t* q_out, u
   }
 }
 
+/* MXFP4 Q preparation: rotation, packing and the weight fold in one op [p2 Changes / Q
+ * quant: the Q op rotates and packs Q to MXFP4 and emits fp32 weights with the softmax
+ * and head scales folded in; p3 Purpose: RoPE covers the leading rope dims of q as of k].
+ * Reading of what the pages leave open:
+ *   - vector v = t * H + h is head h of token t; it is rotated at positions[t] with the
+ *     K store's NeoX rotation (pairs (i, i+32), i < 32, the same cos/sin table, no fused
+ *     operations) applied to the bf16 values as they are (Q gets no normalisation);
+ *     a position outside [0, max_pos) leaves the vector unrotated;
+ *   - the rotated fp64 values are packed exactly as orc_q_quant_mxfp4 packs a vector;
+ *   - w_out[v] = fp32(w[v] * w_scale), w_scale being the product of the factors the
+ *     caller folds in (e.g. head_dim^-1/2 * H^-1/2). */
+void orc_q_prep_mxfp4(const uint16_t* q_bf16, int64_t n_tokens, int32_t H, const int32_t* positions,
+                      const float* cos_sin, int32_t max_pos, const float* w, float w_scale, uint8_t* q_out,
+                      uint8_t* scale_out, float* w_out) {
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    const int32_t pos = positions[t];
+    const int rot = pos >= 0 && pos < max_pos;
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t v = t * H + h;
+      double x[HEAD_DIM], z[HEAD_DIM];
+      for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_double(q_bf16[v * HEAD_DIM + i]);
+      for (int i = 0; i < HEAD_DIM; ++i) z[i] = x[i];
+      if (rot) {
+        const float* cs = cos_sin + (int64_t)pos * 64;
+        for (int i = 0; i < ROPE_DIM / 2; ++i) {
+          double c = (double)cs[i], n = (double)cs[32 + i];
+          double a = x[i], b = x[i + 32];
+          double ac = a * c, bn = b * n, bc = b * c, an = a * n;
+          z[i] = ac - bn;
+          z[i + 32] = bc + an;
+        }
+      }
+      for (int b = 0; b < 4; ++b) orc_mxfp4_quant_block(z + 32 * b, q_out + v * 64 + 16 * b, scale_out + v * 4 + b);
+      w_out[v] = (float)((double)w[v] * (double)w_scale);
+    }
+  }
+}
+
 /* FP8 Q, per-token-group quantisation with group = one 128-dim head vector [p3
  * Purpose: per-token-group FP8 quantisation of q, then the q scale folded into the
  * indexer weights]: sq = fp32(amax / 448), codes e4m3_rne_sat(q_i / sq), and

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libidx.so")
 IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP = 0, -1, -2, -3, -4
 IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
-EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_q_quant_mxfp4", "idx_q_quant_fp8", "idx_logits_paged",
+EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
+           "idx_logits_paged",
            "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_bytes_per_token",
            "idx_device_check", "idx_status_string")
 
@@ -55,6 +56,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_k_store_mxfp4": [PP, V, I64, I64, V, F32, V, V, I32, V, V],
         "idx_k_store_fp8": [PP, V, I64, I64, V, F32, V, V, I32, V, V],
         "idx_q_quant_mxfp4": [V, I64, V, V, V],
+        "idx_q_prep_mxfp4": [V, I64, I32, V, V, I32, V, F32, V, V, V, V],
         "idx_q_quant_fp8": [V, V, I64, V, V, V],
         "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V],
         "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
@@ -114,6 +116,14 @@ def idx_k_store_fp8(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin
     _check("idx_k_store_fp8", load().idx_k_store_fp8(
         ctypes.byref(pool), _ptr(k_bf16), k_bf16.shape[0], k_bf16.stride(0), _ptr(gamma), eps, _ptr(positions),
         _ptr(cos_sin), cos_sin.shape[0], _ptr(slot_mapping), _stream(stream)))
+
+
+def idx_q_prep_mxfp4(q_bf16, positions, cos_sin, w, w_scale: float, q_packed, q_scale, w_out, stream=None):
+    """q_bf16 [T, H, 128] bf16, positions [T] int32, w [T, H] fp32."""
+    T, H = q_bf16.shape[0], q_bf16.shape[1]
+    _check("idx_q_prep_mxfp4", load().idx_q_prep_mxfp4(
+        _ptr(q_bf16), T, H, _ptr(positions), _ptr(cos_sin), cos_sin.shape[0], _ptr(w), w_scale, _ptr(q_packed),
+        _ptr(q_scale), _ptr(w_out), _stream(stream)))
 
 
 def idx_q_quant_mxfp4(q_bf16, q_packed, q_scale, stream=None):

@@ -129,6 +129,33 @@ IDX_EXPORT int idx_k_store_fp8(const idx_pool* pool, const void* k_bf16, int64_t
                         max_pos, slot_mapping, stream);
 }
 
+IDX_EXPORT int idx_q_prep_mxfp4(const void* q_bf16, int64_t n_tokens, int32_t H, const int32_t* positions,
+                                const float* cos_sin, int32_t max_pos, const float* w, float w_scale,
+                                uint8_t* q_packed, uint8_t* q_scale, float* w_out, void* stream) {
+  if (n_tokens < 0 || H < 1 || max_pos <= 0) return IDX_EINVAL;
+  if (H > idx::kMaxHeads) return IDX_EUNSUPPORTED;
+  if (n_tokens > 0 && (!q_bf16 || !positions || !cos_sin || !w || !q_packed || !q_scale || !w_out))
+    return IDX_EINVAL;
+  if (n_tokens > (int64_t)UINT32_MAX / H) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_packed) & 3u) != 0 || (reinterpret_cast<uintptr_t>(q_scale) & 3u) != 0)
+    return IDX_EALIGN;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  idx::QPrepArgs a;
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.n_vecs = n_tokens * H;
+  a.H = H;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.max_pos = max_pos;
+  a.w = w;
+  a.w_scale = w_scale;
+  a.q_out = q_packed;
+  a.q_scale = q_scale;
+  a.w_out = w_out;
+  return hip_status(idx::launch_q_prep_mxfp4(a, static_cast<hipStream_t>(stream)));
+}
+
 IDX_EXPORT int idx_q_quant_mxfp4(const void* q_bf16, int64_t n_vecs, uint8_t* q_packed, uint8_t* q_scale,
                                  void* stream) {
   if (n_vecs < 0) return IDX_EINVAL;

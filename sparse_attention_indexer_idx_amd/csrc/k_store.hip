@@ -1,4 +1,4 @@
-// K-cache store and Q packing for the indexer (gfx950).
+// K-cache store, Q preparation and Q packing for the indexer (gfx950).
 //
 // K store (page "Dense MXFP4 indexer for DeepSeek-V4 on ROCm", Changes / K write:
 // normalise, rotate, pack to MXFP4 and store into the pages in one pass; page
@@ -31,6 +31,23 @@ __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
   }
   kstore_row<FMT>(a.pool, a.k + row * a.row_stride, a.gamma, a.eps, a.cos_sin + (int64_t)pos * 64, slot, lane,
                   nullptr);
+}
+
+// Q preparation for the MXFP4 scorer: rotation of the leading 64 dims at the token's
+// position (the K store's rotation), MXFP4 packing, and the fold of the caller's factor
+// into the weights.  One wave per head vector; a position outside [0, max_pos) leaves
+// the vector unrotated.
+__global__ __launch_bounds__(256) void q_prep_mxfp4_kernel(QPrepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (v >= a.n_vecs) return;
+  const int32_t pos = a.positions[v / a.H];
+  const bool rot = pos >= 0 && pos < a.max_pos;  // wave-uniform
+  const uint16_t* x = a.q + v * 128;
+  const double y0 = bf16_to_f64(x[lane]), y1 = bf16_to_f64(x[lane + 64]);
+  const double z0 = rot ? rope_neox_lane(y0, lane, a.cos_sin + (int64_t)pos * 64) : y0;
+  pack_mxfp4_row(z0, y1, lane, (uint32_t*)(a.q_out + v * 64), (uint32_t*)(a.q_scale + v * 4), nullptr);
+  if (lane == 0) a.w_out[v] = (float)((double)a.w[v] * (double)a.w_scale);
 }
 
 // MXFP4 packing of head vectors: one thread per 32-element block.
@@ -97,6 +114,13 @@ hipError_t launch_k_store(const KStoreArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_store_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_store_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_q_prep_mxfp4(const QPrepArgs& a, hipStream_t s) {
+  if (a.n_vecs == 0) return hipSuccess;
+  const int64_t blocks = (a.n_vecs + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(q_prep_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

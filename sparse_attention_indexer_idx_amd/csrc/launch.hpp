@@ -58,7 +58,23 @@ struct TopkArgs {
   int32_t* out;
 };
 
+// MXFP4 Q preparation: vector v = t*H + h (head h of token t), rotated at positions[t].
+struct QPrepArgs {
+  const uint16_t* q;  // [n_vecs][128] bf16
+  int64_t n_vecs;
+  int32_t H;
+  const int32_t* positions;  // [n_vecs / H]
+  const float* cos_sin;
+  int32_t max_pos;
+  const float* w;  // [n_vecs]
+  float w_scale;
+  uint8_t* q_out;    // [n_vecs][64]
+  uint8_t* q_scale;  // [n_vecs][4]
+  float* w_out;      // [n_vecs]
+};
+
 hipError_t launch_k_store(const KStoreArgs& a, hipStream_t s);
+hipError_t launch_q_prep_mxfp4(const QPrepArgs& a, hipStream_t s);
 hipError_t launch_q_quant_mxfp4(const uint16_t* q, int64_t n_vecs, uint8_t* qp, uint8_t* qs, hipStream_t s);
 hipError_t launch_q_quant_fp8(const uint16_t* q, const float* w, int64_t n_vecs, uint8_t* q8, float* wo,
                               hipStream_t s);

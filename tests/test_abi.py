@@ -160,6 +160,22 @@ def test_decode_step_checks(lib):
         assert step_call(lib) == bd.IDX_EUNSUPPORTED
 
 
+def test_q_prep_checks(lib):
+    f = lambda **kw: lib.idx_q_prep_mxfp4(*[dict(q=FAKE, T=4, H=32, pos=FAKE, cs=FAKE, mp=64, w=FAKE, ws=0.5,
+                                                   qp=FAKE, qs=FAKE, wo=FAKE, st=None, **{})[k] if k not in kw
+                                            else kw[k] for k in ("q", "T", "H", "pos", "cs", "mp", "w", "ws", "qp",
+                                                                 "qs", "wo", "st")])
+    assert f(T=-1) == bd.IDX_EINVAL
+    assert f(H=0) == bd.IDX_EINVAL
+    assert f(H=129) == bd.IDX_EUNSUPPORTED
+    assert f(mp=0) == bd.IDX_EINVAL
+    assert f(pos=None) == bd.IDX_EINVAL
+    assert f(qs=FAKE + 2) == bd.IDX_EALIGN
+    assert f(qp=FAKE + 1) == bd.IDX_EALIGN
+    if no_gpu(lib):
+        assert f() == bd.IDX_EUNSUPPORTED
+
+
 def test_quant_checks(lib):
     assert lib.idx_q_quant_mxfp4(FAKE, -1, FAKE, FAKE, None) == bd.IDX_EINVAL
     assert lib.idx_q_quant_mxfp4(None, 4, FAKE, FAKE, None) == bd.IDX_EINVAL
