@@ -85,7 +85,7 @@ struct NewRows {
       nk.scale = (buf[16] >> (8 * g)) & 0xFFu;
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) nk.v[e] = (int)buf[8 * g + e];
+      for (int e = 0; e < 8; ++e) nk.v[e] = (int)buf[(e < 4 ? 0 : 12) + 4 * g + e];  // dims 16g.., 64+16g..
       nk.scale = buf[32];
     }
     __builtin_amdgcn_wave_barrier();  // the buffer is reused by the next new row

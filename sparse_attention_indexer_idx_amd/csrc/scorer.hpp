@@ -2,10 +2,16 @@
 // step (gfx950): operand tile loads for v_mfma_scale_f32_16x16x128_f8f6f4, the ReLU /
 // weight epilogue, and the decode form's per-wave body.
 //
-// Operand layout: A = 16 head rows of one query (lane l: head l%16, 32-element block
-// l/16, with its E8M0 scale byte), B = 16 cached tokens (lane l: token l%16, block l/16
-// — 16 bytes at token*64 + 16*(l/16), so one wave-wide load covers 16 consecutive tokens
-// = 1 KB contiguous).  Output lane l holds heads 4*(l/16)..+3 of token l%16.
+// Operand layout: A = 16 head rows of one query, B = 16 cached tokens; lane l holds row
+// (head or token) l%16.  Which of the 128 dims a lane's registers hold depends on the
+// element width: with 4-bit elements lane group g = l/16 holds dims [32g, 32g+32) in four
+// registers; with 8-bit elements it holds dims [16g, 16g+16) in registers 0-3 and
+// [64+16g, 64+16g+16) in registers 4-7.  The scale byte a lane supplies applies to dims
+// [32g, 32g+32) in both cases.  Every operand here is loaded so that dim = the
+// instruction's k index (so the scale blocks are the dims' own 32-blocks, and an 8-bit
+// operand may meet a 4-bit one).  MXFP4 K: 16 bytes at token*64 + 16*(l/16), so one
+// wave-wide load covers 16 consecutive tokens = 1 KB contiguous.  Output lane l holds
+// heads 4*(l/16)..+3 of token l%16.
 #pragma once
 
 #include <algorithm>
@@ -52,8 +58,8 @@ __device__ __forceinline__ KTile<FMT> load_k_tile(const uint8_t* __restrict__ pa
     t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
     t.scale = ld<STREAM>(page + ((uint32_t)P * 64u + tok * 4u + g));
   } else {
-    const u32x4* src = (const u32x4*)(page + (tok * 128u + 32u * g));
-    const u32x4 x = ld<STREAM>(src), y = ld<STREAM>(src + 1);
+    const u32x4* src = (const u32x4*)(page + (tok * 128u + 16u * g));
+    const u32x4 x = ld<STREAM>(src), y = ld<STREAM>(src + 4);  // dims 16g.., 64+16g..
     t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
     t.scale = ld<STREAM>((const uint32_t*)(page + ((uint32_t)P * 128u + tok * 4u)));
   }
@@ -74,8 +80,8 @@ __device__ __forceinline__ void load_q_tile(const LogitsArgs& a, int64_t r, int 
     v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
     sc = a.q_scale[vec * 4 + g];
   } else {
-    const uint4* src = (const uint4*)(a.q + vec * 128 + 32 * g);
-    const uint4 x = src[0], y = src[1];
+    const uint4* src = (const uint4*)(a.q + vec * 128 + 16 * g);
+    const uint4 x = src[0], y = src[4];  // dims 16g.., 64+16g..
     v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
     sc = kE8m0One;
   }

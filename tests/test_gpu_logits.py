@@ -82,15 +82,7 @@ def test_logits_large_pool_sampled_rows(fmt):
     check(W, d, logits, seqs, f"cfg4/fmt{fmt}")
 
 
-@pytest.mark.parametrize("H,n_q,P,ctx", [
-    (1, 1, 16, [1, 17, 300]),        # single head, tiny pages
-    (20, 2, 32, [0, 5, 100]),        # ragged head tile, empty sequence, n_q > ctx
-    (48, 1, 256, [700, 513]),        # 3 head tiles, large pages
-    (128, 1, 64, [129, 64]),         # the largest head count
-    (16, 9, 64, [200, 9, 3]),        # 9 head tiles -> the prefill kernel with several sequences
-    (32, 33, 128, [40, 1000]),       # prefill kernel, causal rows crossing chunk edges
-])
-def test_logits_shapes_and_edges(H, n_q, P, ctx):
+def edge_workload(H, n_q, P, ctx, fmt=wl.MXFP4):
     rng = np.random.default_rng(H * 1000 + n_q)
     ctx = np.array(ctx, np.int32)
     B = ctx.size
@@ -105,18 +97,36 @@ def test_logits_shapes_and_edges(H, n_q, P, ctx):
     seq = np.repeat(np.arange(B, dtype=np.int32), ctx)
     posn = np.concatenate([np.arange(int(c), dtype=np.int32) for c in ctx]) if ctx.sum() else np.zeros(0, np.int32)
     slots = pt[seq, posn // P].astype(np.int64) * P + posn % P
-    W = wl.Workload(name="edge", B=B, n_q=n_q, H=H, page_size=P, topk=8, kv_format=wl.MXFP4, ctx=ctx,
-                    num_pages=num_pages, offset_bytes=512, page_stride_bytes=(68 * P + 256 + 255) // 256 * 256, page_table=pt,
+    bpt = 68 if fmt == wl.MXFP4 else 132
+    W = wl.Workload(name="edge", B=B, n_q=n_q, H=H, page_size=P, topk=8, kv_format=fmt, ctx=ctx,
+                    num_pages=num_pages, offset_bytes=512, page_stride_bytes=(bpt * P + 256 + 255) // 256 * 256,
+                    page_table=pt,
                     k_rows=wl.f32_to_bf16_bits(rng.standard_normal((int(ctx.sum()), 128), dtype=np.float32)),
                     k_seq=seq, positions=posn, slots=slots,
                     q_rows=wl.f32_to_bf16_bits(rng.standard_normal((B, n_q, H, 128), dtype=np.float32)),
                     w=(rng.standard_normal((B, n_q, H)) / np.sqrt(H)).astype(np.float32),
                     gamma=np.ones(128, np.float32), eps=1e-6, cos_sin=wl.rope_cos_sin(max(int(ctx.max()), 1)),
                     seed=0)
-    G.say(f"logits edge H={H} n_q={n_q} P={P} ctx={ctx.tolist()}")
-    d = setup_scorer(W, wl.MXFP4)
+    return W
+
+
+@pytest.mark.parametrize("H,n_q,P,ctx,fmt", [
+    (1, 1, 16, [1, 17, 300], wl.MXFP4),        # single head, tiny pages
+    (20, 2, 32, [0, 5, 100], wl.MXFP4),        # ragged head tile, empty sequence, n_q > ctx
+    (48, 1, 256, [700, 513], wl.MXFP4),        # 3 head tiles, large pages
+    (128, 1, 64, [129, 64], wl.MXFP4),         # the largest head count
+    (16, 9, 64, [200, 9, 3], wl.MXFP4),        # 9 head tiles -> the prefill kernel with several sequences
+    (32, 33, 128, [40, 1000], wl.MXFP4),       # prefill kernel, causal rows crossing chunk edges
+    (32, 33, 128, [40, 1000], wl.FP8),         # the same in FP8
+    (20, 17, 64, [17, 700, 0], wl.FP8),        # FP8 prefill, ragged head tile, an empty sequence
+    (128, 5, 64, [300], wl.MXFP4),             # prefill form with 8 head tiles
+])
+def test_logits_shapes_and_edges(H, n_q, P, ctx, fmt):
+    W = edge_workload(H, n_q, P, ctx, fmt)
+    G.say(f"logits edge H={H} n_q={n_q} P={P} ctx={list(ctx)} fmt={fmt}")
+    d = setup_scorer(W, fmt)
     logits = run_scorer(W, d, stride=max(W.max_ctx, 1) + 3)
-    check(W, d, logits, np.arange(W.rows), f"edge H{H} nq{n_q} P{P}")
+    check(W, d, logits, np.arange(W.rows), f"edge H{H} nq{n_q} P{P} fmt{fmt}")
 
 
 def test_bad_page_id_scores_nan_without_faulting():
