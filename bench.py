@@ -524,9 +524,62 @@ def main():
         "topk_hbm_gbs": round(ab["topk"] / (t_mean * 1e-6) / 1e9, 1),
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }
+    result["device"] = device_rates(held, host_s)
+    result["precision_vs_unquantized"] = precision_vs_unquantized(W, logits.cpu().numpy(), out.cpu().numpy())
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, fmt, args.cpu_budget_s)
     print(json.dumps(result), flush=True)
+
+
+def precision_vs_unquantized(W, logits, out, n_rows=4):
+    """This arm's logits and top-k against the method on unquantised operands: bf16 K rows
+    through RMSNorm and NeoX RoPE, bf16 Q, fp32 weights, all in fp64 (no MXFP4 / e4m3
+    rounding).  Cosine over the valid cells and top-k recall, on n_rows sampled rows with
+    more than k valid cells (the longest row of each sampled sequence)."""
+    from sparse_attention_indexer_idx_amd import workloads as wl
+    cand = [r for r in range(W.rows) if W.valid_len(r) > W.topk]
+    if not cand:
+        return None
+    rows = sorted({cand[int(i)] for i in np.linspace(0, len(cand) - 1, n_rows)})
+    offs = W.seq_row_offsets()
+    cos, rec = [], []
+    for r in rows:
+        b, j = divmod(r, W.n_q)
+        n = W.valid_len(r)
+        x = wl.bf16_bits_to_f32(W.k_rows[offs[b]: offs[b] + n]).astype(np.float64)
+        y = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + np.float64(W.eps)) * W.gamma.astype(np.float64)
+        cs = W.cos_sin[W.positions[offs[b]: offs[b] + n]].astype(np.float64)
+        c, sn = cs[:, :32], cs[:, 32:]
+        z = y.copy()
+        z[:, :32] = y[:, :32] * c - y[:, 32:64] * sn
+        z[:, 32:64] = y[:, 32:64] * c + y[:, :32] * sn
+        q = wl.bf16_bits_to_f32(W.q_rows[b, j]).astype(np.float64)          # [H, 128]
+        ref = np.maximum(z @ q.T, 0.0) @ W.w[b, j].astype(np.float64)       # [n]
+        got = logits[r, :n].astype(np.float64)
+        cos.append(float(got @ ref / (np.linalg.norm(got) * np.linalg.norm(ref))))
+        top_ref = np.argsort(-ref, kind="stable")[:W.topk]
+        rec.append(len(np.intersect1d(top_ref, out[r][out[r] >= 0])) / W.topk)
+    return {"rows": rows, "cosine_min": round(min(cos), 7), "topk_recall_min": round(min(rec), 4),
+            "topk_recall_mean": round(float(np.mean(rec)), 4),
+            "reference": "fp64 logits of the unquantised bf16 K (RMSNorm + NeoX RoPE) and Q"}
+
+
+def device_rates(held, host_s):
+    """CU count and peak clock as the runtime reports them, and the sustained rate of the
+    scaled 16x16x128 MFMA on register operands (idx_diag_mfma) next to the nominal peaks."""
+    import torch
+    from sparse_attention_indexer_idx_amd import binding as bd
+    cus, khz = bd.idx_device_info()
+    blocks, rounds = 2048, 2000
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * rounds * 8 * 2 * 16 * 16 * 128
+    rates = {}
+    for name, f in (("fp4", 0), ("fp8", 1)):
+        bd.idx_diag_mfma(f, blocks, rounds, buf)
+        us, _ = held(lambda i: bd.idx_diag_mfma(f, blocks, rounds, buf), 5, host_s)
+        rates[name] = round(flops / (us * 1e-6) / 1e12, 1)
+    return {"cus": cus, "clock_mhz": round(khz / 1000), "mfma_measured_tflops": rates,
+            "mfma_nominal_tflops": {"fp4": FP4_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS}}
 
 
 if __name__ == "__main__":

@@ -266,6 +266,17 @@ size_t idx_decode_step_workspace_bytes(int32_t B);
  * rests on it).  Device fp64 arrays of n elements. */
 int idx_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n, void* stream);
 
+/* Diagnostic: blocks x 256 threads, every wave running 8 * rounds independent scaled
+ * 16x16x128 MFMAs on register operands (fmt 0: E2M1 x E2M1, 1: e4m3 x e4m3), so a
+ * caller timing it gets the sustained matrix rate next to the nominal peak (each MFMA is
+ * 2 * 16 * 16 * 128 flops).  out: device fp32 [blocks * 256] (values meaningless, written
+ * so nothing is dead).  IDX_EINVAL for another fmt, blocks < 1, rounds < 0 or out NULL. */
+int idx_diag_mfma(int32_t fmt, int32_t blocks, int32_t rounds, float* out, void* stream);
+
+/* The current device's compute-unit count and peak shader clock (kHz), as the runtime
+ * reports them.  IDX_EINVAL for a NULL pointer, IDX_EHIP when the runtime query fails. */
+int idx_device_info(int32_t* cus, int32_t* clock_khz);
+
 /* Bytes per token of a format (68, 132), or -1 for an unknown format. */
 int64_t idx_bytes_per_token(int32_t kv_format);
 

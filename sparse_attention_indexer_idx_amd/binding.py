@@ -19,8 +19,8 @@ IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
            "idx_logits_paged",
-           "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_bytes_per_token",
-           "idx_device_check", "idx_status_string")
+           "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_diag_mfma",
+           "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
 
 
 class IdxError(RuntimeError):
@@ -64,6 +64,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                             V, V, ctypes.c_size_t, V],
         "idx_decode_step_workspace_bytes": [I32],
         "idx_diag_fp64": [V, V, V, V, I64, V],
+        "idx_diag_mfma": [I32, I32, I32, V, V],
+        "idx_device_info": [V, V],
         "idx_bytes_per_token": [I32],
         "idx_device_check": [],
         "idx_status_string": [ctypes.c_int],
@@ -170,6 +172,17 @@ def idx_decode_step(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin
 def idx_diag_fp64(a, b, quot, root, stream=None):
     _check("idx_diag_fp64", load().idx_diag_fp64(_ptr(a), _ptr(b), _ptr(quot), _ptr(root), a.numel(),
                                                  _stream(stream)))
+
+
+def idx_diag_mfma(fmt: int, blocks: int, rounds: int, out, stream=None):
+    _check("idx_diag_mfma", load().idx_diag_mfma(fmt, blocks, rounds, _ptr(out), _stream(stream)))
+
+
+def idx_device_info() -> tuple[int, int]:
+    """(compute units, peak shader clock in kHz) of the current device."""
+    cus, khz = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("idx_device_info", load().idx_device_info(ctypes.byref(cus), ctypes.byref(khz)))
+    return cus.value, khz.value
 
 
 def idx_bytes_per_token(kv_format: int) -> int:

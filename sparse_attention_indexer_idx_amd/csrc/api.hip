@@ -293,6 +293,31 @@ IDX_EXPORT int idx_diag_fp64(const double* a, const double* b, double* quot, dou
   return hip_status(idx::launch_diag_fp64(a, b, quot, root, n, static_cast<hipStream_t>(stream)));
 }
 
+IDX_EXPORT int idx_diag_mfma(int32_t fmt, int32_t blocks, int32_t rounds, float* out, void* stream) {
+  if ((fmt != 0 && fmt != 1) || blocks < 1 || rounds < 0 || !out) return IDX_EINVAL;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  return hip_status(idx::launch_diag_mfma(fmt, blocks, rounds, out, static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int idx_device_info(int32_t* cus, int32_t* clock_khz) {
+  if (!cus || !clock_khz) return IDX_EINVAL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return IDX_EHIP;
+  }
+  int c = 0, k = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&k, hipDeviceAttributeClockRate, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return IDX_EHIP;
+  }
+  *cus = c;
+  *clock_khz = k;
+  return IDX_OK;
+}
+
 IDX_EXPORT int64_t idx_bytes_per_token(int32_t kv_format) { return bytes_per_token(kv_format); }
 
 IDX_EXPORT int idx_device_check(void) { return check_device(); }

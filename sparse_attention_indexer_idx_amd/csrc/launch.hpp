@@ -106,6 +106,9 @@ struct StepArgs {
 // sequence, rows of at most 16384 tokens).
 bool decode_step_supported(int n_q, int H, int64_t max_ctx);
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus);
+// 8 * rounds MFMAs (16x16x128, fmt 0: E2M1 x E2M1, 1: e4m3 x e4m3) per wave on register
+// operands; out gets blocks * 256 floats.
+hipError_t launch_diag_mfma(int fmt, int blocks, int rounds, float* out, hipStream_t s);
 hipError_t launch_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n,
                             hipStream_t s);
 

@@ -193,3 +193,11 @@ def test_valid_calls_report_missing_device(lib):
     assert lib.idx_q_quant_mxfp4(FAKE, 4, FAKE, FAKE, None) == bd.IDX_EUNSUPPORTED
     # zero-sized work still goes through the device gate
     assert lib.idx_device_check() == bd.IDX_EUNSUPPORTED
+
+
+def test_diag_mfma_checks(lib):
+    out = ctypes.c_void_p(FAKE)
+    assert lib.idx_diag_mfma(2, 1, 1, out, None) == bd.IDX_EINVAL
+    assert lib.idx_diag_mfma(0, 0, 1, out, None) == bd.IDX_EINVAL
+    assert lib.idx_diag_mfma(1, 1, -1, out, None) == bd.IDX_EINVAL
+    assert lib.idx_diag_mfma(0, 1, 1, None, None) == bd.IDX_EINVAL
