@@ -3,7 +3,9 @@
 A plain fp64 CPU implementation (``idx_oracle.c``) of what the hot path computes:
 the MXFP4 / FP8 codecs, the K-cache store (RMSNorm -> NeoX RoPE -> quantise -> page
 store), the Q packing and the MXFP4 Q preparation (NeoX RoPE -> pack -> weight fold),
-the paged MQA logits with the causal/length mask, and the per-row top-k.
+the FP8 QK preparation (LayerNorm on k, NeoX or interleaved RoPE on q and k, FP8 k to
+the pages, per-vector FP8 q with its scale folded into the weights, padding rows
+zeroed), the paged MQA logits with the causal/length mask, and the per-row top-k.
 Each C function cites the page passage it follows.
 
 Only the test suite, the package smoke check and the benchmark's CPU-baseline leg may
@@ -64,6 +66,8 @@ def _load():
                 "orc_q_quant_mxfp4": (None, [P, I64, P, P]),
                 "orc_q_quant_fp8": (None, [P, P, I64, P, P]),
                 "orc_q_prep_mxfp4": (None, [P, I64, I32, P, P, I32, P, F32, P, P, P]),
+                "orc_qk_prep_fp8": (ctypes.c_int, [P, I64, I64, I64, I32, P, P, I64, I32, P, P, P, I32, I32, P, P,
+                                                   F32, P, P, P]),
                 "orc_valid_len": (I64, [P, I32, I64]),
                 "orc_logits_paged": (ctypes.c_int, [P, I64, I64, I64, I32, I32, P, P, P, P, I32, P, I32, I32, I32,
                                                     P, I64, P, I64]),
@@ -184,6 +188,31 @@ def q_quant_fp8(q_bf16: np.ndarray, w: np.ndarray) -> tuple[np.ndarray, np.ndarr
     q8 = np.empty(q.shape, np.uint8)
     wo = np.empty(w.shape, np.float32)
     _load().orc_q_quant_fp8(_p(q), _p(w), n, _p(q8), _p(wo))
+    return q8, wo
+
+
+def qk_prep_fp8(pool: np.ndarray, offset: int, stride: int, num_pages: int, page_size: int, q_bf16: np.ndarray,
+                k_bf16: np.ndarray, w: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray, neox: bool,
+                ln_gamma: np.ndarray, ln_beta: np.ndarray, eps: float,
+                slots: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 QK preparation: q_bf16 [T, H, 128], k_bf16 [T, 128] uint16, w [T, H] fp32.
+    Writes the K rows into the host FP8 pool in place; returns (q codes [T, H, 128] uint8,
+    w_out [T, H] fp32)."""
+    q_bf16 = np.ascontiguousarray(q_bf16, np.uint16)
+    k_bf16 = np.ascontiguousarray(k_bf16, np.uint16)
+    T, H = q_bf16.shape[0], q_bf16.shape[1]
+    assert q_bf16.shape[2] == 128 and k_bf16.shape == (T, 128) and pool.dtype == np.uint8
+    cos_sin = np.ascontiguousarray(cos_sin, np.float32)
+    q8 = np.empty((T, H, 128), np.uint8)
+    wo = np.empty((T, H), np.float32)
+    rc = _load().orc_qk_prep_fp8(_p(pool), offset, stride, num_pages, page_size, _p(q_bf16), _p(k_bf16), T, H,
+                                 _p(np.ascontiguousarray(w, np.float32)),
+                                 _p(np.ascontiguousarray(positions, np.int32)), _p(cos_sin), cos_sin.shape[0],
+                                 1 if neox else 0, _p(np.ascontiguousarray(ln_gamma, np.float32)),
+                                 _p(np.ascontiguousarray(ln_beta, np.float32)), float(eps),
+                                 _p(np.ascontiguousarray(slots, np.int64)), _p(q8), _p(wo))
+    if rc != 0:
+        raise ValueError("oracle qk_prep_fp8: invalid arguments")
     return q8, wo
 
 

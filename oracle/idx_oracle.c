@@ -329,6 +329,103 @@ void orc_q_quant_fp8(const uint16_t* q_bf16, const float* w, int64_t n_vecs, uin
 }
 
 /* ------------------------------------------------------------------------------ */
+/* FP8 QK preparation: the indexer's five pre-processing steps as one op             */
+/* [p3 Purpose: LayerNorm on k, RoPE on the leading rope dims of q and k, per-token-  */
+/* group FP8 quantisation of q, the q scale folded into the weights, FP8 k written    */
+/* to the paged cache; Test Plan: NeoX and interleaved rotation layouts, page sizes,  */
+/* and the rows the op skips pinned to zero]                                          */
+/* ------------------------------------------------------------------------------ */
+/* Rotation of dims 0..63 of y at the factors cs (32 cosines, then 32 sines); dims
+ * 64..127 pass through.  NeoX pairs (i, i+32); interleaved pairs (2i, 2i+1); pair i
+ * turns by (c_i, n_i) = (cs[i], cs[32+i]), no fused operations:
+ *   first' = first * c - second * n,  second' = second * c + first * n. */
+static void rope64(const double* y, const float* cs, int neox, double* z) {
+  for (int i = 0; i < HEAD_DIM; ++i) z[i] = y[i];
+  for (int i = 0; i < ROPE_DIM / 2; ++i) {
+    const int a_i = neox ? i : 2 * i, b_i = neox ? i + 32 : 2 * i + 1;
+    double c = (double)cs[i], n = (double)cs[32 + i];
+    double a = y[a_i], b = y[b_i];
+    double ac = a * c, bn = b * n, bc = b * c, an = a * n;
+    z[a_i] = ac - bn;
+    z[b_i] = bc + an;
+  }
+}
+
+/* Reading of the steps the page leaves open (fp64 throughout, nothing narrowed before a
+ * code is decided):
+ *   LayerNorm over the 128 dims of k: mu = S(x) / 128, d_i = x_i - mu, var = S(d^2) / 128,
+ *   r = sqrt(var + eps), y_i = (d_i / r) * gamma_i + beta_i, where S sums in the K
+ *   store's fixed order (s_l = v_l + v_{l+64} for l < 64, then s_l = s_l + s_{l+w} for
+ *   w = 32, 16, 8, 4, 2, 1);
+ *   k: rope64, then the FP8 K store's row quantiser (one fp32 scale per token), stored
+ *   at its slot in the 132 B/token page layout;
+ *   q: each head vector of the token rotated as loaded (no normalisation), then
+ *   quantised per 128-dim vector exactly as orc_q_quant_fp8 does, w_out = fp32(w * sq);
+ *   a token whose slot is negative (padding), outside the pool, or whose position is
+ *   outside [0, max_pos) is skipped: no K is stored, and its q codes and weights are
+ *   zero. */
+static double fold_sum(const double* v) {
+  double s[64];
+  for (int l = 0; l < 64; ++l) s[l] = v[l] + v[l + 64];
+  for (int w = 32; w >= 1; w /= 2)
+    for (int l = 0; l < w; ++l) s[l] = s[l] + s[l + w];
+  return s[0];
+}
+
+int orc_qk_prep_fp8(uint8_t* pool, int64_t offset, int64_t stride, int64_t num_pages, int32_t page_size,
+                    const uint16_t* q_bf16, const uint16_t* k_bf16, int64_t n_tokens, int32_t H, const float* w,
+                    const int32_t* positions, const float* cos_sin, int32_t max_pos, int32_t neox,
+                    const float* ln_gamma, const float* ln_beta, float eps, const int64_t* slots, uint8_t* q_out,
+                    float* w_out) {
+  if (page_size <= 0 || H <= 0) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    const int64_t slot = slots[t];
+    const int32_t pos = positions[t];
+    const int skip = slot < 0 || slot / page_size >= num_pages || pos < 0 || pos >= max_pos;
+    if (skip) {
+      memset(q_out + t * H * HEAD_DIM, 0, (size_t)H * HEAD_DIM);
+      for (int32_t h = 0; h < H; ++h) w_out[t * H + h] = 0.0f;
+      continue;
+    }
+    const float* cs = cos_sin + (int64_t)pos * 64;
+    /* k: LayerNorm, rotation, FP8 row, page store */
+    double x[HEAD_DIM], d[HEAD_DIM], sq[HEAD_DIM], y[HEAD_DIM], z[HEAD_DIM];
+    for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_double(k_bf16[t * HEAD_DIM + i]);
+    const double mu = fold_sum(x) / 128.0;
+    for (int i = 0; i < HEAD_DIM; ++i) {
+      d[i] = x[i] - mu;
+      sq[i] = d[i] * d[i];
+    }
+    const double r = sqrt(fold_sum(sq) / 128.0 + (double)eps);
+    for (int i = 0; i < HEAD_DIM; ++i) {
+      const double nrm = (d[i] / r) * (double)ln_gamma[i];
+      y[i] = nrm + (double)ln_beta[i];
+    }
+    rope64(y, cs, neox, z);
+    uint8_t* page = pool + offset + (slot / page_size) * stride;
+    const int64_t row = slot % page_size;
+    float sk;
+    fp8_quant_row(z, page + row * 128, &sk);
+    memcpy(page + (int64_t)page_size * 128 + row * 4, &sk, 4);
+    /* q: rotation, per-vector FP8, weight fold */
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t v = t * H + h;
+      double qx[HEAD_DIM], qz[HEAD_DIM], amax = 0.0;
+      for (int i = 0; i < HEAD_DIM; ++i) qx[i] = bf16_to_double(q_bf16[v * HEAD_DIM + i]);
+      rope64(qx, cs, neox, qz);
+      for (int i = 0; i < HEAD_DIM; ++i)
+        if (fabs(qz[i]) > amax) amax = fabs(qz[i]);
+      const float s = (float)(amax / 448.0);
+      for (int i = 0; i < HEAD_DIM; ++i)
+        q_out[v * HEAD_DIM + i] = (s == 0.0f) ? (signbit(qz[i]) ? 0x80 : 0x00) : orc_e4m3_encode(qz[i] / (double)s);
+      w_out[v] = (float)((double)w[v] * (double)s);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
 /* Scorer: paged MQA logits with the causal / length mask                           */
 /* ------------------------------------------------------------------------------ */
 /* Row r = b * n_q + j holds query token j of sequence b.  Its valid length is
