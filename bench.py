@@ -525,6 +525,7 @@ def main():
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }
     result["device"] = device_rates(held, host_s)
+    result["qk_prep_fp8_us"] = qk_prep_fp8_times(held, host_s, args.steps)
     result["precision_vs_unquantized"] = precision_vs_unquantized(W, logits.cpu().numpy(), out.cpu().numpy())
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, fmt, args.cpu_budget_s)
@@ -562,6 +563,39 @@ def precision_vs_unquantized(W, logits, out, n_rows=4):
     return {"rows": rows, "cosine_min": round(min(cos), 7), "topk_recall_min": round(min(rec), 4),
             "topk_recall_mean": round(float(np.mean(rec)), 4),
             "reference": "fp64 logits of the unquantised bf16 K (RMSNorm + NeoX RoPE) and Q"}
+
+
+def qk_prep_fp8_times(held, host_s, steps):
+    """idx_qk_prep_fp8 (LayerNorm k, interleaved RoPE on q and k, FP8 q with the scale
+    folded into the weights, FP8 k to the pages) for 1 and 1024 tokens at 32 heads and
+    page size 64, each timed alone back to back; not part of the step."""
+    import torch
+    from sparse_attention_indexer_idx_amd import binding as bd
+    from sparse_attention_indexer_idx_amd import workloads as wl
+    out = {}
+    rng = np.random.default_rng(53)
+    for T in (1, 1024):
+        H, P, max_pos = 32, 64, 8192
+        n_pages = (T + P - 1) // P + 1
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        pool = torch.zeros(n_pages * 132 * P, dtype=torch.uint8, device="cuda")
+        view = bd.make_pool(pool, 0, 132 * P, n_pages, P, wl.FP8)
+        q = dev(wl.f32_to_bf16_bits(rng.standard_normal((T, H, 128), dtype=np.float32)).view(np.int16)).view(
+            torch.bfloat16)
+        k = dev(wl.f32_to_bf16_bits(rng.standard_normal((T, 128), dtype=np.float32)).view(np.int16)).view(
+            torch.bfloat16)
+        w = dev(rng.standard_normal((T, H), dtype=np.float32))
+        pos = dev(rng.integers(0, max_pos, T).astype(np.int32))
+        slots = dev(rng.permutation(n_pages * P)[:T].astype(np.int64))
+        cs = dev(wl.rope_cos_sin(max_pos))
+        g, b = torch.ones(128, device="cuda"), torch.zeros(128, device="cuda")
+        q8 = torch.empty((T, H, 128), dtype=torch.uint8, device="cuda")
+        wo = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        f = lambda i: bd.idx_qk_prep_fp8(view, q, k, w, pos, cs, False, g, b, 1e-6, slots, q8, wo)
+        f(0)
+        us, _ = held(f, steps, host_s)
+        out[str(T)] = round(us, 3)
+    return out
 
 
 def device_rates(held, host_s):

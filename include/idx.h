@@ -155,6 +155,34 @@ int idx_q_prep_mxfp4(const void* q_bf16, int64_t n_tokens, int32_t H, const int3
                      int32_t max_pos, const float* w, float w_scale, uint8_t* q_packed, uint8_t* q_scale, float* w_out,
                      void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * FP8 QK preparation in one launch (page "[ROCm][Perf] Fuse DSA indexer QK preprocessing
+ * with AITER", Purpose: the indexer's five pre-processing steps — LayerNorm on k, RoPE on
+ * the leading rope dims of q and k, per-token-group FP8 quantisation of q, the q scale
+ * folded into the weights, FP8 quantisation of k with the paged cache write — as one
+ * kernel; Test Plan: NeoX and interleaved rotation layouts, and the rows the op skips
+ * left at zero).  For token t (all arithmetic fp64, no fused operations):
+ *   k: mu = S(x)/128, d = x - mu, r = sqrt(S(d^2)/128 + eps), y = (d / r) * ln_gamma +
+ *      ln_beta (S sums in the K store's fold-then-halve order); dims 0..63 rotated at
+ *      positions[t] (below); FP8 row as idx_k_store_fp8 (sk = fp32(amax/448), e4m3
+ *      codes) stored at slot_mapping[t] of the FP8 pool;
+ *   q: each head vector [t][h] rotated as loaded, then sq = fp32(amax/448), codes
+ *      e4m3(q/sq) to q_fp8[t][h], w_out[t][h] = fp32(w[t][h] * sq) (idx_q_quant_fp8);
+ *   rotation: pairs (i, i+32) when rope_neox = 1, (2i, 2i+1) when 0, i < 32; pair i
+ *      turns by (cos_sin[pos][i], cos_sin[pos][32+i]): a' = a c - b n, b' = b c + a n;
+ *   a token whose slot is negative (padding), outside the pool, or whose position is
+ *      outside [0, max_pos) is skipped: no K is stored, its q_fp8 bytes and w_out are 0.
+ * pool: FP8 (IDX_EINVAL otherwise).  q_bf16 device bf16 [n_tokens][H][128]; k_bf16 device
+ * bf16 [n_tokens][128]; w, w_out device fp32 [n_tokens][H] (w_out may alias w);
+ * positions int32 [n_tokens]; cos_sin fp32 [max_pos][64]; ln_gamma, ln_beta fp32 [128];
+ * eps > 0; slot_mapping int64 [n_tokens]; q_fp8 device uint8 [n_tokens][H][128], 4-byte
+ * aligned.  n_tokens >= 0 (0 is a no-op); H in [1, 128]; n_tokens * (H + 1) < 2^26.
+ * ------------------------------------------------------------------------------- */
+int idx_qk_prep_fp8(const idx_pool* pool, const void* q_bf16, const void* k_bf16, int64_t n_tokens, int32_t H,
+                    const float* w, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                    int32_t rope_neox, const float* ln_gamma, const float* ln_beta, float eps,
+                    const int64_t* slot_mapping, uint8_t* q_fp8, float* w_out, void* stream);
+
 /* FP8 Q with one scale per 128-dim head vector, multiplied into that head's weight
  * (page "[ROCm][Perf] Fuse DSA indexer QK preprocessing with AITER", Purpose: q is FP8
  * quantised per token group and its scale is then folded into the indexer weights):

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libidx.so")
 IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP = 0, -1, -2, -3, -4
 IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
-EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
+EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_qk_prep_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
            "idx_logits_paged",
            "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_diag_mfma",
            "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
@@ -57,6 +57,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_k_store_fp8": [PP, V, I64, I64, V, F32, V, V, I32, V, V],
         "idx_q_quant_mxfp4": [V, I64, V, V, V],
         "idx_q_prep_mxfp4": [V, I64, I32, V, V, I32, V, F32, V, V, V, V],
+        "idx_qk_prep_fp8": [PP, V, V, I64, I32, V, V, V, I32, I32, V, V, F32, V, V, V, V],
         "idx_q_quant_fp8": [V, V, I64, V, V, V],
         "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V],
         "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
@@ -132,6 +133,17 @@ def idx_q_quant_mxfp4(q_bf16, q_packed, q_scale, stream=None):
     n = q_bf16.numel() // 128
     _check("idx_q_quant_mxfp4", load().idx_q_quant_mxfp4(_ptr(q_bf16), n, _ptr(q_packed), _ptr(q_scale),
                                                          _stream(stream)))
+
+
+def idx_qk_prep_fp8(pool: IdxPool, q_bf16, k_bf16, w, positions, cos_sin, neox: bool, ln_gamma, ln_beta,
+                    eps: float, slot_mapping, q_fp8, w_out, stream=None):
+    """q_bf16 [T, H, 128] and k_bf16 [T, 128] bf16, w [T, H] fp32 -> q_fp8 [T, H, 128] uint8,
+    w_out [T, H] fp32, and the K rows stored into the FP8 pool."""
+    T, H = q_bf16.shape[0], q_bf16.shape[1]
+    _check("idx_qk_prep_fp8", load().idx_qk_prep_fp8(
+        ctypes.byref(pool), _ptr(q_bf16), _ptr(k_bf16), T, H, _ptr(w), _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], 1 if neox else 0, _ptr(ln_gamma), _ptr(ln_beta), eps, _ptr(slot_mapping), _ptr(q_fp8),
+        _ptr(w_out), _stream(stream)))
 
 
 def idx_q_quant_fp8(q_bf16, w, q_fp8, w_out, stream=None):

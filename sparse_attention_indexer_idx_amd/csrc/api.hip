@@ -129,6 +129,42 @@ IDX_EXPORT int idx_k_store_fp8(const idx_pool* pool, const void* k_bf16, int64_t
                         max_pos, slot_mapping, stream);
 }
 
+IDX_EXPORT int idx_qk_prep_fp8(const idx_pool* pool, const void* q_bf16, const void* k_bf16, int64_t n_tokens,
+                               int32_t H, const float* w, const int32_t* positions, const float* cos_sin,
+                               int32_t max_pos, int32_t rope_neox, const float* ln_gamma, const float* ln_beta,
+                               float eps, const int64_t* slot_mapping, uint8_t* q_fp8, float* w_out, void* stream) {
+  int st = check_pool(pool, IDX_KV_FP8_E4M3);
+  if (st != IDX_OK) return st;
+  if (n_tokens < 0 || H < 1 || max_pos <= 0 || !(eps > 0.0f) || (rope_neox != 0 && rope_neox != 1))
+    return IDX_EINVAL;
+  if (H > idx::kMaxHeads) return IDX_EUNSUPPORTED;
+  if (n_tokens > 0 && (!q_bf16 || !k_bf16 || !w || !positions || !cos_sin || !ln_gamma || !ln_beta ||
+                       !slot_mapping || !q_fp8 || !w_out))
+    return IDX_EINVAL;
+  // one wave per vector: the grid's work-items (64 per vector) must fit in 32 bits
+  if (n_tokens > (int64_t)(UINT32_MAX / 64) / (H + 1)) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_fp8) & 3u) != 0) return IDX_EALIGN;
+  if ((st = check_device()) != IDX_OK) return st;
+  idx::QKPrepArgs a;
+  a.pool = view_of(pool);
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.k = static_cast<const uint16_t*>(k_bf16);
+  a.n_tokens = n_tokens;
+  a.H = H;
+  a.w = w;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.max_pos = max_pos;
+  a.neox = rope_neox;
+  a.ln_gamma = ln_gamma;
+  a.ln_beta = ln_beta;
+  a.eps = (double)eps;
+  a.slots = slot_mapping;
+  a.q_out = q_fp8;
+  a.w_out = w_out;
+  return hip_status(idx::launch_qk_prep_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 IDX_EXPORT int idx_q_prep_mxfp4(const void* q_bf16, int64_t n_tokens, int32_t H, const int32_t* positions,
                                 const float* cos_sin, int32_t max_pos, const float* w, float w_scale,
                                 uint8_t* q_packed, uint8_t* q_scale, float* w_out, void* stream) {

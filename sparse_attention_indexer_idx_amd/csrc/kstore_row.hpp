@@ -67,10 +67,10 @@ __device__ __forceinline__ void pack_mxfp4_row(double z0, double z1, int lane, u
 }
 
 // FP8 row: one fp32 scale, sk = fp32(amax / 448), codes e4m3(z / sk) (sign-only zeros
-// when sk == 0).  Writes the 32 code words and the scale, and the same 33 words to `copy`
-// when it is non-null.
-__device__ __forceinline__ void pack_fp8_row(double z0, double z1, int lane, uint32_t* __restrict__ code_words,
-                                             float* __restrict__ scale, uint32_t* copy) {
+// when sk == 0).  Writes the 32 code words and (when `scale` is non-null) the scale, and
+// the same 33 words to `copy` when it is non-null; returns sk on every lane.
+__device__ __forceinline__ float pack_fp8_row(double z0, double z1, int lane, uint32_t* __restrict__ code_words,
+                                              float* __restrict__ scale, uint32_t* copy) {
 #pragma clang fp contract(off)
   double m = fmax(fabs(z0), fabs(z1));
 #pragma unroll
@@ -100,9 +100,10 @@ __device__ __forceinline__ void pack_fp8_row(double z0, double z1, int lane, uin
     }
   }
   if (lane == 0) {
-    *scale = sk;
+    if (scale) *scale = sk;
     if (copy) copy[32] = __float_as_uint(sk);
   }
+  return sk;
 }
 
 // Store row xr (128 bf16) at pool slot `slot` (already checked to lie in the pool), with

@@ -37,6 +37,27 @@ struct KStoreArgs {
   int32_t step_max_ctx = 0;
 };
 
+// FP8 QK preparation: T tokens, H query heads per token.
+struct QKPrepArgs {
+  PoolView pool;          // FP8 pool
+  const uint16_t* q;      // bf16 [T][H][128]
+  const uint16_t* k;      // bf16 [T][128]
+  int64_t n_tokens;
+  int32_t H;
+  const float* w;         // [T][H]
+  const int32_t* positions;
+  const float* cos_sin;   // [max_pos][64]
+  int32_t max_pos;
+  int32_t neox;           // 1: pairs (i, i+32); 0: pairs (2i, 2i+1)
+  const float* ln_gamma;  // [128]
+  const float* ln_beta;   // [128]
+  double eps;
+  const int64_t* slots;
+  uint8_t* q_out;         // e4m3 [T][H][128]
+  float* w_out;           // [T][H]
+};
+hipError_t launch_qk_prep_fp8(const QKPrepArgs& a, hipStream_t s);
+
 struct LogitsArgs {
   PoolView pool;
   const uint8_t* q;

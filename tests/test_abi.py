@@ -201,3 +201,32 @@ def test_diag_mfma_checks(lib):
     assert lib.idx_diag_mfma(0, 0, 1, out, None) == bd.IDX_EINVAL
     assert lib.idx_diag_mfma(1, 1, -1, out, None) == bd.IDX_EINVAL
     assert lib.idx_diag_mfma(0, 1, 1, None, None) == bd.IDX_EINVAL
+
+
+def qk_prep_call(lib, p=None, **kw):
+    a = dict(q=FAKE, k=FAKE, T=4, H=8, w=FAKE, pos=FAKE, cs=FAKE, max_pos=16, neox=1, g=FAKE, b=FAKE, eps=1e-6,
+             slots=FAKE, q8=FAKE, wo=FAKE)
+    a.update(kw)
+    p = p or pool(kv_format=1, page_stride_bytes=132 * 64)
+    return lib.idx_qk_prep_fp8(ctypes.byref(p), a["q"], a["k"], a["T"], a["H"], a["w"], a["pos"], a["cs"],
+                               a["max_pos"], a["neox"], a["g"], a["b"], a["eps"], a["slots"], a["q8"], a["wo"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(H=0), bd.IDX_EINVAL),
+    (dict(H=129), bd.IDX_EUNSUPPORTED),
+    (dict(T=-1), bd.IDX_EINVAL),
+    (dict(neox=2), bd.IDX_EINVAL),
+    (dict(eps=0.0), bd.IDX_EINVAL),
+    (dict(max_pos=0), bd.IDX_EINVAL),
+    (dict(k=None), bd.IDX_EINVAL),
+    (dict(q8=FAKE + 2), bd.IDX_EALIGN),
+    (dict(T=(1 << 26) // 9 + 1), bd.IDX_EINVAL),   # the grid would pass 2^32 work-items
+])
+def test_qk_prep_checks(lib, kw, want):
+    assert qk_prep_call(lib, **kw) == want
+
+
+def test_qk_prep_needs_an_fp8_pool(lib):
+    assert qk_prep_call(lib, p=pool()) == bd.IDX_EINVAL
+
