@@ -5,7 +5,8 @@ the MXFP4 / FP8 codecs, the K-cache store (RMSNorm -> NeoX RoPE -> quantise -> p
 store), the Q packing and the MXFP4 Q preparation (NeoX RoPE -> pack -> weight fold),
 the FP8 QK preparation (LayerNorm on k, NeoX or interleaved RoPE on q and k, FP8 k to
 the pages, per-vector FP8 q with its scale folded into the weights, padding rows
-zeroed), the paged MQA logits with the causal/length mask, and the per-row top-k.
+zeroed), the paged MQA logits with the causal/length mask, the per-row top-k, and both
+restricted to a row's candidate blocks.
 Each C function cites the page passage it follows.
 
 Only the test suite, the package smoke check and the benchmark's CPU-baseline leg may
@@ -258,6 +259,48 @@ def logits_exact(q_rows: np.ndarray, w: np.ndarray, k_rows: np.ndarray, ctx: np.
 
 
 # ----------------------------------------------------------------------------- top-k
+def candidate_cells(cand_blocks: np.ndarray, page_size: int, max_pages: int, ctx: np.ndarray, n_q: int):
+    """Token index and validity of every candidate cell: row r, candidate j, cell i is
+    token cand_blocks[r, j] * P + i, valid when the block id lies in [0, max_pages) and
+    the token is below the row's valid length.  Returns (tokens [rows, n_cand*P] int64,
+    valid bool of the same shape).  Reading of the two-level indexer's second level
+    ([p2] Purpose: the candidate-pool path scores only the candidate blocks of a row):
+    a candidate block is a page-sized run of the sequence's tokens, named by its index in
+    the sequence's page table."""
+    cand = np.asarray(cand_blocks, np.int64)
+    rows, n_cand = cand.shape
+    i = np.arange(page_size, dtype=np.int64)
+    tok = (cand[:, :, None] * page_size + i[None, None, :]).reshape(rows, n_cand * page_size)
+    n = np.array([valid_len(ctx, n_q, r) for r in range(rows)], np.int64)
+    ok = ((cand >= 0) & (cand < max_pages))[:, :, None].repeat(page_size, axis=2).reshape(rows, -1)
+    return tok, ok & (tok < n[:, None]) & (tok >= 0)
+
+
+def logits_candidates(dense_logits: np.ndarray, cand_blocks: np.ndarray, page_size: int, max_pages: int,
+                      ctx: np.ndarray, n_q: int) -> np.ndarray:
+    """The scorer restricted to candidate cells: cell (r, j*P + i) holds the plain logit of
+    its token (dense_logits from logits_paged for every row), -inf where the cell is not
+    a valid candidate."""
+    tok, ok = candidate_cells(cand_blocks, page_size, max_pages, ctx, n_q)
+    out = np.full(tok.shape, -np.inf)
+    r = np.nonzero(ok)
+    out[r] = dense_logits[r[0], tok[r]]
+    return out
+
+
+def topk_candidates(cand_logits: np.ndarray, cand_blocks: np.ndarray, page_size: int, max_pages: int,
+                    ctx: np.ndarray, n_q: int, k: int) -> np.ndarray:
+    """Per row, the k tokens with the largest logits among the valid candidate cells
+    (ties to the smaller token index), then -1."""
+    tok, ok = candidate_cells(cand_blocks, page_size, max_pages, ctx, n_q)
+    out = np.full((tok.shape[0], k), -1, np.int32)
+    for r in range(tok.shape[0]):
+        v, t = cand_logits[r][ok[r]], tok[r][ok[r]]
+        order = np.lexsort((t, -v))[:k]
+        out[r, :order.size] = t[order]
+    return out
+
+
 def topk(logits: np.ndarray, ctx: np.ndarray, n_q: int, k: int, rows: np.ndarray | None = None) -> np.ndarray:
     """Indices [len(rows), k] in rank order (logit desc, index asc), -1 padded.
 
