@@ -249,6 +249,43 @@ int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens
              int32_t max_ctx, int32_t k, int32_t* out_idx, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Candidate-block scorer: the second level of a two-level indexer, where each query
+ * row scores only the blocks a first level chose for it (page "Dense MXFP4 indexer for
+ * DeepSeek-V4 on ROCm", Purpose: the candidate-pool path beside the dense one, which is
+ * the same scorer called with no candidate blocks).  The pages do not define a candidate
+ * block; here it is one page-sized run of the row's sequence, named by its index in the
+ * sequence's page table, and read in place from the page that entry names.
+ *
+ * Row r = b * n_q + j (valid length n_r as for idx_logits_paged) has candidate ids
+ * cand_blocks[r * n_cand + c], c < n_cand (negative = padding).  Every cell
+ * c * P + i (i < P) of the row's logits is written:
+ *   logits[r * logits_stride + c*P + i] = the idx_logits_paged logit of token
+ *       s = cand * P + i  when 0 <= cand < max_pages_per_seq and s < n_r,
+ *   = -inf otherwise (padding ids, ids past the page table, tokens past n_r).
+ * A page id outside the pool scores NaN, as in idx_logits_paged.  The ids of a row
+ * should be distinct (a repeated id repeats its cells).
+ * Arguments as for idx_logits_paged (max_ctx is not taken: the candidate count bounds
+ * the cells), plus cand_blocks device int32 [B * n_q][n_cand] and n_cand >= 0;
+ * n_cand * P <= logits_stride, n_cand * P <= 65536 (IDX_EUNSUPPORTED beyond) and
+ * max_pages_per_seq * P < 2^31.
+ * ------------------------------------------------------------------------------- */
+int idx_logits_candidates(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                          const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
+                          int32_t n_q, int32_t H, int32_t D, const int32_t* cand_blocks, int32_t n_cand,
+                          float* logits, int64_t logits_stride, void* stream);
+
+/* Per-row top-k over candidate cells (the logits idx_logits_candidates writes): cells
+ * holding -inf are not candidates; among the others, the k with the largest logits, as
+ * token indices cand_blocks[r][c] * P + i.  A row with at most k candidate cells outputs
+ * all of their tokens, then -1.  Equal logits go to the earlier cell (the smaller token
+ * when a row's ids ascend); the order within a row is unspecified but deterministic.
+ * logits device fp32 [B * n_q][logits_stride]; cand_blocks device int32 [B * n_q][n_cand];
+ * page_size P as the pool's; n_cand * P <= logits_stride and <= 65536; k >= 1;
+ * out_idx device int32 [B * n_q][k]. */
+int idx_topk_candidates(const float* logits, int64_t logits_stride, const int32_t* cand_blocks, int32_t n_cand,
+                        int32_t page_size, int32_t B, int32_t n_q, int32_t k, int32_t* out_idx, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Fused decode step: the K store of the step's new rows, the scorer and the top-k in
  * one launch.  The pages run these as separate launches per indexer layer (page "Dense
  * MXFP4 indexer for DeepSeek-V4 on ROCm", Changes: the K write, then the MQA-logits

@@ -18,7 +18,7 @@ IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP = 0, -1, -2, -3, -4
 IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_qk_prep_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
-           "idx_logits_paged",
+           "idx_logits_paged", "idx_logits_candidates", "idx_topk_candidates",
            "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_diag_mfma",
            "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
 
@@ -61,6 +61,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_q_quant_fp8": [V, V, I64, V, V, V],
         "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V],
         "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
+        "idx_logits_candidates": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, V, I32, V, I64, V],
+        "idx_topk_candidates": [V, I64, V, I32, I32, I32, I32, I32, V, V],
         "idx_decode_step": [PP, V, I64, V, F32, V, V, I32, V, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, I32,
                             V, V, ctypes.c_size_t, V],
         "idx_decode_step_workspace_bytes": [I32],
@@ -157,6 +159,21 @@ def idx_logits_paged(pool: IdxPool, q, q_scale, w, page_table, ctx_lens, B: int,
     _check("idx_logits_paged", load().idx_logits_paged(
         ctypes.byref(pool), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1], _ptr(ctx_lens),
         B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), _stream(stream)))
+
+
+def idx_logits_candidates(pool: IdxPool, q, q_scale, w, page_table, ctx_lens, B: int, n_q: int, H: int, cand_blocks,
+                          logits, stream=None):
+    """cand_blocks: int32 [B*n_q][n_cand] block (page-table) indices, negative = padding;
+    logits: fp32 [B*n_q][>= n_cand*P]."""
+    _check("idx_logits_candidates", load().idx_logits_candidates(
+        ctypes.byref(pool), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1], _ptr(ctx_lens),
+        B, n_q, H, 128, _ptr(cand_blocks), cand_blocks.shape[1], _ptr(logits), logits.stride(0), _stream(stream)))
+
+
+def idx_topk_candidates(logits, cand_blocks, page_size: int, B: int, n_q: int, k: int, out_idx, stream=None):
+    _check("idx_topk_candidates", load().idx_topk_candidates(
+        _ptr(logits), logits.stride(0), _ptr(cand_blocks), cand_blocks.shape[1], page_size, B, n_q, k, _ptr(out_idx),
+        _stream(stream)))
 
 
 def idx_topk(logits, ctx_lens, B: int, n_q: int, max_ctx: int, k: int, out_idx, stream=None):

@@ -285,6 +285,53 @@ IDX_EXPORT int idx_topk(const float* logits, int64_t logits_stride, const int32_
   return hip_status(idx::launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
+IDX_EXPORT int idx_logits_candidates(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                                     const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
+                                     int32_t B, int32_t n_q, int32_t H, int32_t D, const int32_t* cand_blocks,
+                                     int32_t n_cand, float* logits, int64_t logits_stride, void* stream) {
+  if (!pool) return IDX_EINVAL;
+  if (n_cand < 0 || (n_cand > 0 && !cand_blocks)) return IDX_EINVAL;
+  const int64_t cells = (int64_t)n_cand * pool->page_size;
+  if (cells > logits_stride) return IDX_EINVAL;
+  // token indices (block id * P + row) must fit an int32
+  if ((int64_t)max_pages_per_seq * pool->page_size > (int64_t)INT32_MAX) return IDX_EINVAL;
+  if (cells > idx::kTopkMaxCtx) return IDX_EUNSUPPORTED;
+  idx::LogitsArgs a;
+  // max_ctx is not used by this entry point (cells are bounded by the candidate count)
+  int st = logits_args(pool, q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, 0, logits,
+                       logits_stride, a);
+  if (st != IDX_OK) return st;
+  if ((st = check_device()) != IDX_OK) return st;
+  idx::CandArgs c;
+  c.cand = cand_blocks;
+  c.n_cand = n_cand;
+  return hip_status(idx::launch_logits_candidates(a, c, static_cast<hipStream_t>(stream)));
+}
+
+IDX_EXPORT int idx_topk_candidates(const float* logits, int64_t logits_stride, const int32_t* cand_blocks,
+                                   int32_t n_cand, int32_t page_size, int32_t B, int32_t n_q, int32_t k,
+                                   int32_t* out_idx, void* stream) {
+  if (!logits || !out_idx || n_cand < 0 || (n_cand > 0 && !cand_blocks)) return IDX_EINVAL;
+  if (B < 1 || n_q < 1 || k < 1 || logits_stride < 1) return IDX_EINVAL;
+  if (page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)) != 0) return IDX_EUNSUPPORTED;
+  const int64_t cells = (int64_t)n_cand * page_size;
+  if (cells > logits_stride) return IDX_EINVAL;
+  if ((int64_t)B * n_q > (int64_t)INT32_MAX) return IDX_EINVAL;
+  if (cells > idx::kTopkMaxCtx) return IDX_EUNSUPPORTED;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  idx::TopkCandArgs a;
+  a.logits = logits;
+  a.lstride = logits_stride;
+  a.cand = cand_blocks;
+  a.n_cand = n_cand;
+  a.page_shift = __builtin_ctz((unsigned)page_size);
+  a.rows = (int64_t)B * n_q;
+  a.k = k;
+  a.out = out_idx;
+  return hip_status(idx::launch_topk_candidates(a, static_cast<hipStream_t>(stream)));
+}
+
 IDX_EXPORT size_t idx_decode_step_workspace_bytes(int32_t B) {
   if (B < 1) return 0;
   return ((size_t)B * sizeof(int32_t) + 255) / 256 * 256;

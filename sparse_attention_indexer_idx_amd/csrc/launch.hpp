@@ -107,6 +107,28 @@ bool logits_uses_decode_kernel(int n_q, int H);
 int64_t logits_max_ctx(int n_q, int H, int page_size);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
+// Candidate blocks of each query row: cand[r][c] is a block (page-table) index of row
+// r's sequence, negative = padding.  Cell c*P + i of the row's logits is token
+// cand[r][c]*P + i.
+struct CandArgs {
+  const int32_t* cand;  // [rows][n_cand]
+  int32_t n_cand;
+};
+hipError_t launch_logits_candidates(const LogitsArgs& a, const CandArgs& c, hipStream_t s);
+
+// Top-k over candidate cells: row r has n_cand*P cells; -inf cells are not candidates.
+struct TopkCandArgs {
+  const float* logits;
+  int64_t lstride;
+  const int32_t* cand;
+  int32_t n_cand;
+  int32_t page_shift;
+  int64_t rows;
+  int32_t k;
+  int32_t* out;
+};
+hipError_t launch_topk_candidates(const TopkCandArgs& a, hipStream_t s);
+
 // The fused decode step: K store of the B*n_q new rows, scorer, top-k, in one launch.
 // Row i = b*n_q + j of k/positions/slots is token ctx[b] - n_q + j of sequence b.
 struct StepArgs {

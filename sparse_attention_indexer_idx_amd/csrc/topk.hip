@@ -17,6 +17,33 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   topk_row<NT, EPT>(a.logits + r * a.lstride, n, a.k, a.out + r * a.k, sh);
 }
 
+// Candidate rows: n_cand*P cells, -inf cells are not candidates, cells map to tokens
+// through the row's candidate block ids.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_cand_kernel(TopkCandArgs a) {
+  __shared__ TopkShared<NT, EPT> sh;
+  const int64_t r = blockIdx.x;
+  CandidateRow map;
+  map.cand = a.cand + r * a.n_cand;
+  map.page_shift = a.page_shift;
+  topk_row<NT, EPT, CandidateRow>(a.logits + r * a.lstride, a.n_cand << a.page_shift, a.k, a.out + r * a.k, sh,
+                                  map);
+}
+
+template <int NT>
+hipError_t launch_cand_nt(const TopkCandArgs& a, int ept, hipStream_t s) {
+  const dim3 grid((unsigned)a.rows);
+  switch (ept) {
+#define IDX_TOPK_CASE(E) \
+  case E: hipLaunchKernelGGL((topk_cand_kernel<NT, E>), grid, dim3(NT), 0, s, a); break;
+    IDX_TOPK_CASE(1) IDX_TOPK_CASE(2) IDX_TOPK_CASE(4) IDX_TOPK_CASE(8) IDX_TOPK_CASE(16) IDX_TOPK_CASE(32)
+    IDX_TOPK_CASE(64)
+#undef IDX_TOPK_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int NT>
 hipError_t launch_nt(const TopkArgs& a, int ept, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.B * a.n_q));
@@ -33,14 +60,30 @@ hipError_t launch_nt(const TopkArgs& a, int ept, hipStream_t s) {
 
 }  // namespace
 
+// Block size by rows per CU, as for the dense rows.
+int topk_block_size(int64_t rows, int64_t cells) {
+  if (rows >= 4 * 256 && cells <= 256 * 32) return 256;
+  if (rows > 256 && cells <= 512 * 32) return 512;
+  return 1024;
+}
+
+hipError_t launch_topk_candidates(const TopkCandArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  const int64_t cells = (int64_t)a.n_cand << a.page_shift;
+  const int nt = topk_block_size(a.rows, cells);
+  int ept = 1;
+  while ((int64_t)ept * nt < cells) ept *= 2;
+  if (nt == 256) return launch_cand_nt<256>(a, ept, s);
+  if (nt == 512) return launch_cand_nt<512>(a, ept, s);
+  return launch_cand_nt<1024>(a, ept, s);
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
   // Rows per CU decides the block size: with many rows, 256-thread blocks let several
   // rows share a CU; with about one row per CU, 1024 threads shorten each row's chain.
-  int nt = 1024;
-  if (rows >= 4 * 256 && a.max_ctx <= 256 * 32) nt = 256;
-  else if (rows > 256 && a.max_ctx <= 512 * 32) nt = 512;
+  const int nt = topk_block_size(rows, a.max_ctx);
   int ept = 1;
   while ((int64_t)ept * nt < a.max_ctx) ept *= 2;
   if (nt == 256) return launch_nt<256>(a, ept, s);

@@ -133,17 +133,38 @@ __device__ __forceinline__ void select_digit(SH& sh, int kk) {
   __syncthreads();
 }
 
-// Top-k of one row by one workgroup of NT threads: `row` holds n valid cells (n <= NT*EPT),
-// the k selected indices (or 0..n-1 then -1 when n <= k) go to out[0..k).  Every thread
-// of the block calls it with the same arguments.
-template <int NT, int EPT>
+// How a row's cells become keys and output indices.  DenseRow: every cell below n is
+// valid and is its own token index.  CandidateRow: cell c*P + i is token
+// cand[c]*P + i, and a cell holding -inf is not a candidate (the candidate scorer writes
+// -inf there), so the number of valid cells is only known once the keys are formed.
+struct DenseRow {
+  static constexpr bool kCountValid = false;
+  __device__ __forceinline__ uint32_t key(float f) const { return float_key(f); }
+  __device__ __forceinline__ int32_t token(int cell) const { return cell; }
+};
+
+struct CandidateRow {
+  static constexpr bool kCountValid = true;
+  const int32_t* cand;
+  int32_t page_shift;
+  __device__ __forceinline__ uint32_t key(float f) const { return f == -__builtin_inff() ? 0u : float_key(f); }
+  __device__ __forceinline__ int32_t token(int cell) const {
+    return (cand[cell >> page_shift] << page_shift) + (cell & ((1 << page_shift) - 1));
+  }
+};
+
+// Top-k of one row by one workgroup of NT threads: `row` holds n cells (n <= NT*EPT), the
+// k selected token indices go to out[0..k); when the row has at most k valid cells, all
+// of them are output, then -1 (DenseRow: 0..n-1).  Ties go to the earlier cell.  Every
+// thread of the block calls it with the same arguments.
+template <int NT, int EPT, class Map = DenseRow>
 __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
-                                         TopkShared<NT, EPT>& sh) {
+                                         TopkShared<NT, EPT>& sh, const Map map = Map()) {
   using C = Cfg<NT>;
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (n <= k) {
-    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? i : -1;
+  if (n <= (Map::kCountValid ? 0 : k)) {  // uniform
+    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? map.token(i) : -1;
     return;
   }
   const int ne = (n + NT - 1) / NT;  // rounds that hold valid cells (uniform)
@@ -155,7 +176,23 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
   uint32_t key[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) key[e] = (e * NT + tid < n) ? float_key(raw[e]) : 0u;
+  for (int e = 0; e < EPT; ++e) key[e] = (e * NT + tid < n) ? map.key(raw[e]) : 0u;
+  if constexpr (Map::kCountValid) {
+    // At most k valid cells: all of them, in cell order, then -1.  (The scan's barrier
+    // also orders the histogram clear; wave_tot is next written after pass 1's barrier.)
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) cnt += key[e] != 0u ? 1 : 0;
+    int total;
+    int pos = block_excl_scan<NT>(cnt, sh.wave_tot, total);
+    if (total <= k) {  // uniform
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        if (key[e] != 0u) out[pos++] = map.token(e * NT + tid);
+      for (int i = total + tid; i < k; i += NT) out[i] = -1;
+      return;
+    }
+  }
   __syncthreads();
 
   // ---- pass 1: the top D1 bits of every valid cell ----
@@ -205,12 +242,12 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
         for (; t < nc; t += G) cnt += sh.cand[t] > me ? 1 : 0;
       }
       for (int m = 1; m < G; m <<= 1) cnt += shfl_xor(cnt, m);
-      if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = (int32_t)~(uint32_t)me;
+      if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = map.token((int)~(uint32_t)me);
     }
     // cells above the bucket: after the barriers, so no store is waited for
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
-      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = e * NT + tid;
+      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
     return;
   }
 
@@ -285,7 +322,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
       const int gt_before = sh.cnt_gt[e * NW + wave] + __popcll(bg & lt);
       const int eq_before = sh.cnt_eq[e * NW + wave] + __popcll(be & lt);
       const int pos = gt_before + min(eq_before, need_eq);
-      if ((is_gt || (is_eq && eq_before < need_eq)) && pos < k) out[pos] = i;
+      if ((is_gt || (is_eq && eq_before < need_eq)) && pos < k) out[pos] = map.token(i);
     }
   }
 }

@@ -242,3 +242,24 @@ def random_logits(rng: np.random.Generator, rows: int, stride: int, *, ties: boo
         return rng.standard_normal(size=(rows, stride), dtype=np.float32)
     vals = np.array([-2.0, -1.0, -0.0, 0.0, 0.5, 1.0, 3.0], np.float32)
     return vals[rng.integers(0, vals.size, size=(rows, stride))]
+
+
+def candidate_blocks(rng: np.random.Generator, W: Workload, n_cand: int, *, pad: int = 0,
+                     past_table: int = 0, shuffled: bool = False) -> np.ndarray:
+    """Candidate block ids [rows, n_cand] int32 for the candidate-block scorer: per row,
+    distinct block (page-table) indices of its sequence drawn without replacement from
+    the blocks that hold tokens (ascending unless `shuffled`); when a sequence has fewer
+    blocks, the rest are padding (-1).  `pad` entries per row are then replaced by -1 and
+    `past_table` by ids at or past the page-table width (edge cases)."""
+    P, mp = W.page_size, W.page_table.shape[1]
+    out = np.full((W.rows, n_cand), -1, np.int32)
+    for r in range(W.rows):
+        nb = min(mp, -(-int(W.ctx[r // W.n_q]) // P))
+        m = min(n_cand, nb)
+        ids = rng.choice(nb, m, replace=False) if m else np.zeros(0, np.int64)
+        out[r, :m] = np.sort(ids) if not shuffled else ids
+        if pad:
+            out[r, rng.choice(n_cand, pad, replace=False)] = -1
+        if past_table:
+            out[r, rng.choice(n_cand, past_table, replace=False)] = mp + rng.integers(0, 3, past_table)
+    return out

@@ -230,3 +230,42 @@ def test_qk_prep_checks(lib, kw, want):
 def test_qk_prep_needs_an_fp8_pool(lib):
     assert qk_prep_call(lib, p=pool()) == bd.IDX_EINVAL
 
+
+
+def cand_call(lib, p=None, **kw):
+    """idx_logits_candidates with valid-looking fake pointers (B2, H4, 4 blocks of 64)."""
+    a = dict(q=FAKE, qs=FAKE, w=FAKE, pt=FAKE, maxp=4, ctx=FAKE, B=2, n_q=1, H=4, D=128, cand=FAKE, nc=4,
+             logits=FAKE, lstride=256)
+    a.update(kw)
+    p = p or pool()
+    return lib.idx_logits_candidates(ctypes.byref(p), a["q"], a["qs"], a["w"], a["pt"], a["maxp"], a["ctx"], a["B"],
+                                     a["n_q"], a["H"], a["D"], a["cand"], a["nc"], a["logits"],
+                                     ctypes.c_int64(a["lstride"]), None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=64), bd.IDX_EUNSUPPORTED),
+    (dict(H=0), bd.IDX_EINVAL),
+    (dict(nc=-1), bd.IDX_EINVAL),
+    (dict(cand=None), bd.IDX_EINVAL),
+    (dict(lstride=255), bd.IDX_EINVAL),                       # fewer than n_cand * P cells
+    (dict(nc=1025, lstride=1 << 20), bd.IDX_EUNSUPPORTED),   # more than 65536 cells
+    (dict(maxp=1 << 25), bd.IDX_EINVAL),                      # token ids past int32
+    (dict(qs=None), bd.IDX_EINVAL),
+    (dict(q=FAKE + 8), bd.IDX_EALIGN),
+])
+def test_candidate_argument_checks(lib, kw, want):
+    assert cand_call(lib, **kw) == want
+
+
+def test_topk_candidate_checks(lib):
+    f = lib.idx_topk_candidates
+    assert f(None, 256, FAKE, 4, 64, 2, 1, 64, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 256, None, 4, 64, 2, 1, 64, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 255, FAKE, 4, 64, 2, 1, 64, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 256, FAKE, 4, 48, 2, 1, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
+    assert f(FAKE, 256, FAKE, 4, 64, 2, 1, 0, FAKE, None) == bd.IDX_EINVAL
+    assert f(FAKE, 1 << 20, FAKE, 1025, 64, 2, 1, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
+    if no_gpu(lib):
+        assert cand_call(lib) == bd.IDX_EUNSUPPORTED
+        assert f(FAKE, 256, FAKE, 4, 64, 2, 1, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
