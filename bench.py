@@ -404,6 +404,24 @@ def main():
         qprep_us, _ = held(lambda i: bd.idx_q_prep_mxfp4(q3, qpos, cos_sin, w, 0.0625, qp2, qs2, w2), args.steps,
                            host_s)
 
+    cand_us = None
+    if decode_form(W):
+        # The candidate-block scorer and its top-k (a two-level indexer's second level):
+        # every row scores 16 blocks of its sequence drawn without replacement (seeded),
+        # over the same rotated pool replicas; not part of the step.
+        n_cand = min(16, W.page_table.shape[1])
+        cand = dev(wl.candidate_blocks(np.random.default_rng(77), W, n_cand))
+        clog = torch.empty((W.rows, n_cand * P), dtype=torch.float32, device="cuda")
+        cout = torch.empty((W.rows, W.topk), dtype=torch.int32, device="cuda")
+        cs_mean, _ = held(lambda i: bd.idx_logits_candidates(pools[i % replicas][1], q, qs, w, pt, ctx, W.B, W.n_q, W.H,
+                                                             cand, clog), args.steps, host_s)
+        ct_mean, _ = held(lambda i: bd.idx_topk_candidates(clog, cand, P, W.B, W.n_q, W.topk, cout), args.steps,
+                          host_s)
+        cells = W.rows * n_cand * P
+        cbytes = cells * (68 if fmt == 0 else 132) // max(W.n_q, 1) + cells * 4 + W.rows * n_cand * 4
+        cand_us = {"blocks_per_row": n_cand, "score": round(cs_mean, 3), "topk": round(ct_mean, 3),
+                   "score_hbm_gbs": round(cbytes / (cs_mean * 1e-6) / 1e9, 1)}
+
     # The step captured into HIP graphs, as a serving loop runs the indexer inside a
     # captured forward pass: graph A holds L consecutive steps (L a multiple of the replica
     # count, at least 8, so a replay's fixed launch cost is shared as it is across the
@@ -521,6 +539,7 @@ def main():
         "roofline": roof if fused_us is None else fused_roof,
         "scorer_roofline": roof,
         "q_prep_us": None if qprep_us is None else round(qprep_us, 3),
+        "candidates_us": cand_us,
         "topk_hbm_gbs": round(ab["topk"] / (t_mean * 1e-6) / 1e9, 1),
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }
