@@ -39,6 +39,21 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
   decode_wave<FMT, NT, G>(a, blockIdx.y, tok0, threadIdx.x & 63, none);
 }
 
+// Row-split decode kernel for several query rows with many heads (e.g. 3 speculative
+// tokens x 64 heads): each wave holds one query row's head tiles instead of all rows', so
+// registers stay low enough for several waves per SIMD; the n_q blocks that share a token
+// range are adjacent in launch order, so the rows after the first read K from cache.
+// Waves past their sequence leave early (these shapes come with mixed lengths).
+// Grid = (ceil(max_ctx / (256*G)) * n_q, B).
+template <int FMT, int HT, int G>
+__global__ __launch_bounds__(256) void logits_decode_rows_kernel(LogitsArgs a) {
+  const int wave = uniform(threadIdx.x >> 6);
+  const int j = blockIdx.x % a.n_q, chunk = blockIdx.x / a.n_q;
+  const int tok0 = (chunk * kDecodeWaves + wave) * (64 * G);
+  NoPatch none;
+  decode_wave<FMT, HT, G, NoPatch, true>(a, blockIdx.y, tok0, threadIdx.x & 63, none, j);
+}
+
 // ------------------------------------------------------------------------------------
 // Prefill / long query sets: each wave owns 4 query rows (one per lane group after the
 // transpose-reduce) and walks 16-token K tiles; a block is 4 waves = 16 rows.  Work
@@ -168,10 +183,29 @@ hipError_t launch_decode_g(const LogitsArgs& a, int nt, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int FMT, int G>
+hipError_t launch_decode_rows_g(const LogitsArgs& a, int ht, hipStream_t s) {
+  const int tok_per_block = kDecodeWaves * 64 * G;
+  const dim3 grid((unsigned)((a.max_ctx + tok_per_block - 1) / tok_per_block * a.n_q), (unsigned)a.B);
+  switch (ht) {
+#define IDX_ROWS_CASE(N) \
+  case N: hipLaunchKernelGGL((logits_decode_rows_kernel<FMT, N, G>), grid, dim3(256), 0, s, a); break;
+    IDX_ROWS_CASE(1) IDX_ROWS_CASE(2) IDX_ROWS_CASE(3) IDX_ROWS_CASE(4)
+    IDX_ROWS_CASE(5) IDX_ROWS_CASE(6) IDX_ROWS_CASE(7) IDX_ROWS_CASE(8)
+#undef IDX_ROWS_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Two 64-token groups per wave while the query tiles leave room in registers: each wave
-// then carries twice the K bytes per page-table and Q round trip.
+// then carries twice the K bytes per page-table and Q round trip.  Several query rows
+// with more than four head tiles in all are split one row per wave.
 template <int FMT>
 hipError_t launch_decode(const LogitsArgs& a, int nt, hipStream_t s) {
+  const int ht = (a.H + kHeadTile - 1) / kHeadTile;
+  if (a.n_q > 1 && nt > 4)
+    return ht <= 4 ? launch_decode_rows_g<FMT, 2>(a, ht, s) : launch_decode_rows_g<FMT, 1>(a, ht, s);
   return nt <= 4 ? launch_decode_g<FMT, 2>(a, nt, s) : launch_decode_g<FMT, 1>(a, nt, s);
 }
 

@@ -158,25 +158,31 @@ struct NoPatch {
   }
 };
 
-template <int FMT, int NT, int G, class Patch>
-__device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, Patch& patch) {
+// The wave scores query rows j_base .. j_base + NT/HT - 1 of sequence b (all n_q rows when
+// j_base = 0 and NT = n_q * HT; one row when NT = HT).  EXIT_DEAD: a wave wholly past its
+// sequence leaves before its K loads (worth it where many waves are: many heads and mixed
+// lengths); the price is that the compiler then issues the Q loads after the page-table
+// round trip instead of before it.
+template <int FMT, int NT, int G, class Patch, bool EXIT_DEAD = false>
+__device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, Patch& patch,
+                                            int j_base = 0) {
   constexpr int T = 4 * G;  // K tiles per wave
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int last_page = (a.max_ctx - 1) >> lgP;
   const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
 
   // Q and w first: they do not depend on the page table and come from L2, so they are
-  // in registers by the time the K bytes arrive.  The kernel has no early exit: a wave
-  // past the end of the context reads page 0 row 0 for every tile (an L2 hit shared by
-  // all such waves) and stores nothing, so no branch stands between these loads and the
-  // page-table round trip.
+  // in registers by the time the K bytes arrive.  Without EXIT_DEAD there is no early
+  // exit: a wave past the end of the context reads page 0 row 0 for every tile (an L2
+  // hit shared by all such waves) and stores nothing, so no branch stands between these
+  // loads and the page-table round trip.
   const int HT = (a.H + kHeadTile - 1) / kHeadTile;
   v8i qa[NT];
   uint32_t qs[NT];
   v4f qw[NT];
 #pragma unroll
   for (int m = 0; m < NT; ++m) {
-    const int j = m / HT, ht = m % HT;
+    const int j = j_base + m / HT, ht = m % HT;
     const int64_t r = (int64_t)b * a.n_q + j;
     load_q_tile<FMT>(a, r, ht, lane, qa[m], qs[m]);
     qw[m] = load_w_tile(a, r, ht, lane);
@@ -189,6 +195,7 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
   const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
   const bool live = tok0 < n_b;  // n_b <= max_ctx, so this also covers waves past max_ctx
   patch.prepare(n_b);
+  if (EXIT_DEAD && !live) return;  // nothing to store
 
   // K tiles: a tile of a dead wave or on an invalid page reads page 0 row 0 (always
   // inside the pool); invalid pages score NaN below, dead waves store nothing.
@@ -232,7 +239,7 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
           const float v = FMT == 1 ? acc[t] * __uint_as_float(k4[t].scale) : acc[t];
           p[t] = ok4[t] ? v : qnan;
         }
-        emit(m / HT, reduce4_transpose(p[0], p[1], p[2], p[3]));
+        emit(j_base + m / HT, reduce4_transpose(p[0], p[1], p[2], p[3]));
       }
     }
   };
