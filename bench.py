@@ -189,7 +189,7 @@ def summarize(dirs, traffic_key=None, calib_mib=0):
         if not vals:
             raise SystemExit(f"no {counter} rows for the requested kernel")
         return reduce(vals)
-    scorer = lambda k: k.startswith("logits_")
+    scorer = lambda k: k.startswith("logits_") and not k.startswith("logits_cand")
     copy = lambda k: "copyBuffer" in k
     big = lambda vals: max(vals, key=lambda t: t[2])  # the largest grid = the timed launches
     known_kib = calib_mib * 1024.0

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
 // Row-split decode kernel for several query rows with many heads (e.g. 3 speculative
 // tokens x 64 heads): each wave holds one query row's head tiles instead of all rows', so
 // registers stay low enough for several waves per SIMD; the n_q blocks that share a token
-// range are adjacent in launch order, so the rows after the first read K from cache.
+// range are adjacent in launch order, and K is loaded as cacheable lines, so the rows
+// after the first read K from cache.
 // Waves past their sequence leave early (these shapes come with mixed lengths).
 // Grid = (ceil(max_ctx / (256*G)) * n_q, B).
 template <int FMT, int HT, int G>
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(256) void logits_decode_rows_kernel(LogitsArgs a) {
   const int j = blockIdx.x % a.n_q, chunk = blockIdx.x / a.n_q;
   const int tok0 = (chunk * kDecodeWaves + wave) * (64 * G);
   NoPatch none;
-  decode_wave<FMT, HT, G, NoPatch, true>(a, blockIdx.y, tok0, threadIdx.x & 63, none, j);
+  decode_wave<FMT, HT, G, NoPatch, true, false>(a, blockIdx.y, tok0, threadIdx.x & 63, none, j);
 }
 
 // ------------------------------------------------------------------------------------

@@ -162,8 +162,9 @@ struct NoPatch {
 // j_base = 0 and NT = n_q * HT; one row when NT = HT).  EXIT_DEAD: a wave wholly past its
 // sequence leaves before its K loads (worth it where many waves are: many heads and mixed
 // lengths); the price is that the compiler then issues the Q loads after the page-table
-// round trip instead of before it.
-template <int FMT, int NT, int G, class Patch, bool EXIT_DEAD = false>
+// round trip instead of before it.  STREAM_K: K loads are non-temporal (read once per
+// call); off where several waves read the same tiles from the cache.
+template <int FMT, int NT, int G, class Patch, bool EXIT_DEAD = false, bool STREAM_K = true>
 __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, Patch& patch,
                                             int j_base = 0) {
   constexpr int T = 4 * G;  // K tiles per wave
@@ -207,7 +208,7 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
     const bool valid_page = pid[t] >= 0 && (int64_t)pid[t] < a.pool.num_pages;
     const bool use = live && valid_page;
     const uint8_t* page = a.pool.base + (use ? (int64_t)pid[t] : 0) * a.pool.stride;
-    kt[t] = load_k_tile<FMT, true>(page, P, use ? (s0 & (P - 1)) : 0, lane);
+    kt[t] = load_k_tile<FMT, STREAM_K>(page, P, use ? (s0 & (P - 1)) : 0, lane);
     ok[t] = valid_page;  // tiles past n_b are computed but never stored
   }
 
