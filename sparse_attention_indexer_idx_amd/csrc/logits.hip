@@ -41,16 +41,18 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
 
 // Row-split decode kernel for several query rows with many heads (e.g. 3 speculative
 // tokens x 64 heads): each wave holds one query row's head tiles instead of all rows', so
-// registers stay low enough for several waves per SIMD; the n_q blocks that share a token
-// range are adjacent in launch order, and K is loaded as cacheable lines, so the rows
-// after the first read K from cache.
-// Waves past their sequence leave early (these shapes come with mixed lengths).
-// Grid = (ceil(max_ctx / (256*G)) * n_q, B).
+// registers stay low enough for several waves per SIMD.  The waves of a block take rows
+// 4i..4i+3 of one token range, so K is fetched from memory once per CU and the other
+// rows read it from the cache (rows past n_q leave at once).  Waves past their sequence
+// leave early too (these shapes come with mixed lengths).
+// Grid = (ceil(max_ctx / (64*G)) * ceil(n_q / 4), B).
 template <int FMT, int HT, int G>
 __global__ __launch_bounds__(256) void logits_decode_rows_kernel(LogitsArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
-  const int j = blockIdx.x % a.n_q, chunk = blockIdx.x / a.n_q;
-  const int tok0 = (chunk * kDecodeWaves + wave) * (64 * G);
+  const int rb = (a.n_q + 3) >> 2;
+  const int chunk = blockIdx.x / rb, j = (blockIdx.x - chunk * rb) * 4 + wave;
+  if (j >= a.n_q) return;
+  const int tok0 = chunk * (64 * G);
   NoPatch none;
   decode_wave<FMT, HT, G, NoPatch, true, false>(a, blockIdx.y, tok0, threadIdx.x & 63, none, j);
 }
@@ -186,8 +188,8 @@ hipError_t launch_decode_g(const LogitsArgs& a, int nt, hipStream_t s) {
 
 template <int FMT, int G>
 hipError_t launch_decode_rows_g(const LogitsArgs& a, int ht, hipStream_t s) {
-  const int tok_per_block = kDecodeWaves * 64 * G;
-  const dim3 grid((unsigned)((a.max_ctx + tok_per_block - 1) / tok_per_block * a.n_q), (unsigned)a.B);
+  const int tok_per_block = 64 * G;
+  const dim3 grid((unsigned)((a.max_ctx + tok_per_block - 1) / tok_per_block * ((a.n_q + 3) / 4)), (unsigned)a.B);
   switch (ht) {
 #define IDX_ROWS_CASE(N) \
   case N: hipLaunchKernelGGL((logits_decode_rows_kernel<FMT, N, G>), grid, dim3(256), 0, s, a); break;

@@ -154,3 +154,28 @@ def test_topk_candidates_isolated_exact(rows, n_cand, P, k, ties):
         assert np.array_equal(np.sort(g[g >= 0]), np.sort(o[o >= 0])), f"row {r}"
         m = int((o >= 0).sum())
         assert np.all(g[m:] == -1) and np.all(g[:m] >= 0), f"row {r}"
+
+
+@pytest.mark.parametrize("fmt", [wl.MXFP4, wl.FP8])
+def test_candidates_large_pool_sampled_rows(fmt):
+    """The 6 GiB pool whose used pages straddle 2 GiB, 4 GiB, 4608 MiB and 4.608e9 B: the
+    candidate scorer rebases each page in 64 bits like the dense one."""
+    W = wl.make_workload(4, kv_format=fmt)
+    strad = set(wl.straddling_pages(max(W.page_stride_bytes, W.page_bytes)))
+    seqs = sorted(b for b in range(W.B) if strad & set(W.page_table[b].tolist()))
+    G.say(f"candidates large pool fmt={fmt}, sequences {seqs}")
+    rng = np.random.default_rng(321 + fmt)
+    cand = wl.candidate_blocks(rng, W, 24)
+    # the straddling pages' blocks among the candidates of their sequences' rows
+    for b in seqs:
+        blocks = [i for i, p in enumerate(W.page_table[b].tolist()) if p in strad]
+        others = [int(x) for x in cand[b] if x >= 0 and x not in blocks]
+        row = sorted(blocks + others[: cand.shape[1] - len(blocks)])
+        cand[b] = -1
+        cand[b, :len(row)] = row
+    rows = np.unique(np.concatenate([seqs, [0, W.B - 1]])).astype(np.int64)
+    d = setup_scorer(W, fmt)
+    logits = run_cand(W, d, cand)
+    ref = check_cand(W, d, cand, logits, rows, f"cand large pool fmt{fmt}")
+    got = gpu_topk_cand(logits, cand, W.page_size, W.B, W.n_q, W.topk)[rows]
+    check_topk_cand(W, cand, got, ref, rows, W.topk, f"cand topk large pool fmt{fmt}")
