@@ -109,26 +109,20 @@ __device__ __forceinline__ void block_excl_scan2(int v0, int v1, int32_t* wave_t
 
 // Given a histogram of BINS digits (BINS >= NT), find the digit d holding the kk-th
 // largest item (kk >= 1): count(digits > d) < kk <= count(digits >= d).  Thread t covers
-// BINS/NT digits, the highest to thread 0, and keeps them in registers, so the thread
-// whose range holds the answer finds it without another LDS round trip.  Leaves d and
-// count(> d) in shared memory (two barriers).
+// BINS/NT digits, the highest to thread 0; only the thread whose range holds the answer
+// re-reads its bins.  Leaves d and count(> d) in shared memory (two barriers).
 template <int NT, int BINS, class SH>
 __device__ __forceinline__ void select_digit(SH& sh, int kk) {
   constexpr int PER = BINS / NT;
   const int hi = BINS - PER * (int)threadIdx.x;  // digits [hi - PER, hi)
-  int bins[PER];
   int local = 0;
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    bins[q] = (int)sh.hist[hi - 1 - q];
-    local += bins[q];
-  }
+  for (int q = 0; q < PER; ++q) local += (int)sh.hist[hi - 1 - q];
   int total;
   int before = block_excl_scan<NT>(local, sh.wave_tot, total);
   if (before < kk && kk <= before + local) {
-#pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int c = bins[q];
+      const int c = (int)sh.hist[hi - 1 - q];
       if (before < kk && kk <= before + c) {
         sh.sel_digit = hi - 1 - q;
         sh.sel_above = before;
