@@ -179,3 +179,40 @@ def test_candidates_large_pool_sampled_rows(fmt):
     ref = check_cand(W, d, cand, logits, rows, f"cand large pool fmt{fmt}")
     got = gpu_topk_cand(logits, cand, W.page_size, W.B, W.n_q, W.topk)[rows]
     check_topk_cand(W, cand, got, ref, rows, W.topk, f"cand topk large pool fmt{fmt}")
+
+
+def test_candidates_graph_replay_matches_eager():
+    """Candidate scorer + candidate top-k captured in a HIP graph: every replay reproduces
+    the eager results bit for bit."""
+    torch = G.torch_cuda()
+    W = wl.make_workload(3)
+    cand = G.dev(wl.candidate_blocks(np.random.default_rng(331), W, 12, pad=1))
+    d = setup_scorer(W, wl.MXFP4)
+    logits = torch.zeros((W.rows, 12 * W.page_size), dtype=torch.float32, device="cuda")
+    out = torch.zeros((W.rows, W.topk), dtype=torch.int32, device="cuda")
+
+    def step():
+        bd.idx_logits_candidates(d["pool"].view, d["q_d"], d["qs_d"], d["w_d"], d["pt_d"], d["ctx_d"], W.B, W.n_q,
+                                 W.H, cand, logits)
+        bd.idx_topk_candidates(logits, cand, W.page_size, W.B, W.n_q, W.topk, out)
+
+    G.say("candidates graph replay cfg=3")
+    step()
+    torch.cuda.synchronize()
+    ref_logits, ref_out = logits.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        logits.fill_(5.0)
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits.view(torch.int32), ref_logits.view(torch.int32)), f"replay {rep}: logits"
+        assert torch.equal(out, ref_out), f"replay {rep}: top-k"

@@ -182,3 +182,44 @@ def test_step_skips_rows_before_the_first_token(cfg, scale):
     after = st.pool.read_pages(np.array([pid]))
     assert np.array_equal(before, after), "a row with a negative token index was stored"
     assert np.all(out[1] == -1), "the empty sequence's row must be all -1"
+
+
+def test_step_graph_replay_matches_eager():
+    """The fused step captured in a HIP graph: every replay (eager work and a sync between
+    replays) reproduces the eager call's pool bytes, logits bits and indices, and leaves the
+    workspace zero (the kernel resets its own counters, so no memset node is needed)."""
+    torch = G.torch_cuda()
+    W = wl.make_workload(1)
+    ctx = np.asarray(W.ctx, np.int32)
+    new = new_rows(W, ctx)
+    old = np.setdiff1d(np.arange(W.k_rows.shape[0]), new[new >= 0])
+    st = Step(W, wl.MXFP4, ctx, G.CompactHostPool(W, wl.MXFP4, rows=old))
+    logits, out = st.buffers()
+
+    def step():
+        bd.idx_decode_step(st.pool.view, st.k_d, st.gamma_d, W.eps, st.pos_d, st.cs_d, st.slot_d, st.q_d, st.qs_d,
+                           st.w_d, st.pt_d, st.ctx_d, W.B, W.n_q, W.H, W.max_ctx, logits, W.topk, out, st.ws)
+
+    G.say("fused step graph replay cfg=1")
+    step()
+    torch.cuda.synchronize()
+    ref_pool, ref_logits, ref_out = st.pool.base.clone(), logits.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        logits.copy_(ref_logits)
+        logits[:, :64].fill_(3.0)   # cells every row rewrites
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bool((st.pool.base == ref_pool).all()), f"replay {rep}: pool"
+        assert torch.equal(logits.view(torch.int32), ref_logits.view(torch.int32)), f"replay {rep}: logits"
+        assert torch.equal(out, ref_out), f"replay {rep}: top-k"
+        assert int(st.ws.abs().sum().item()) == 0, f"replay {rep}: workspace"
