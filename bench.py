@@ -393,6 +393,8 @@ def main():
     k_mean, k_us = held(k_store, args.steps, host_s)
     s_mean, s_us = held(score, args.steps, host_s)
     t_mean, t_us = held(topk, args.steps, host_s)
+    # the scorer on one pool replica over and over: K then sits in the last-level cache
+    w_mean, _ = held(lambda i: score(0), args.steps, host_s)
     qprep_us = None
     if fmt == 0:
         # The Q-side preparation that feeds the scorer (rotation + MXFP4 packing + weight
@@ -533,7 +535,9 @@ def main():
                          "score_p10_p90": [round(float(np.percentile(s_us, 10)), 3),
                                            round(float(np.percentile(s_us, 90)), 3)],
                          "score_plus_topk": round(s_mean + t_mean, 3),
-                         "note": "each kernel alone, back to back; per-call mean (p10/p90 over groups of 10 calls)"},
+                         "score_warm": round(w_mean, 3),
+                         "note": "each kernel alone, back to back; per-call mean (p10/p90 over groups of 10 calls); "
+                                 "score_warm: the scorer on one pool replica (K resident in the last-level cache)"},
         # the step's kernel: the fused decode step when the step runs through it, else the
         # scorer (the dominant one of the three); the scorer alone is always listed too
         "roofline": roof if fused_us is None else fused_roof,

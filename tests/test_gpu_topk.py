@@ -37,6 +37,9 @@ def gpu_topk(logits_d, ctx, B, n_q, max_ctx, k):
     (1100, 1, (1024, 5000), 1024, True),     # 256-thread variant, ties in the boundary bucket
     (700, 1, (1000, 4096), 300, False),      # short rows, small k
     (600, 1, (1000, 9000), 1024, False),     # 512-thread variant, 32 cells per thread
+    (2100, 1, (1, 8192), 1024, True),        # many rows, heavy ties
+    (2600, 2, (900, 5000), 300, False),      # many rows, n_q 2, small k
+    (2048, 1, (16000, 16384), 1024, True),   # many long rows with ties
 ])
 def test_topk_isolated_exact(rows, n_q, lens, k, ties):
     rng = np.random.default_rng(rows * 7 + k + int(ties))
