@@ -144,7 +144,7 @@ int idx_q_quant_mxfp4(const void* q_bf16, int64_t n_vecs, uint8_t* q_packed, uin
  * unrotated.  w_out[v] = fp32(w[v] * w_scale), where w_scale is the product of the
  * factors folded in (for example head_dim^-1/2 * H^-1/2).
  *
- * q_bf16     device bf16 [n_tokens][H][128];  positions device int32 [n_tokens];
+ * q_bf16     device bf16 [n_tokens][H][128], 16-byte aligned;  positions device int32 [n_tokens];
  * cos_sin    device fp32 [max_pos][64] (32 cosines, 32 sines per position);
  * w          device fp32 [n_tokens][H];  w_out device fp32 [n_tokens][H];
  * q_packed   device uint8 [n_tokens][H][64], 4-byte aligned;

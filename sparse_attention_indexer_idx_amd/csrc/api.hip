@@ -173,7 +173,8 @@ IDX_EXPORT int idx_q_prep_mxfp4(const void* q_bf16, int64_t n_tokens, int32_t H,
   if (n_tokens > 0 && (!q_bf16 || !positions || !cos_sin || !w || !q_packed || !q_scale || !w_out))
     return IDX_EINVAL;
   if (n_tokens > (int64_t)UINT32_MAX / H) return IDX_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(q_packed) & 3u) != 0 || (reinterpret_cast<uintptr_t>(q_scale) & 3u) != 0)
+  if ((reinterpret_cast<uintptr_t>(q_packed) & 3u) != 0 || (reinterpret_cast<uintptr_t>(q_scale) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(q_bf16) & 15u) != 0)
     return IDX_EALIGN;
   int st = check_device();
   if (st != IDX_OK) return st;

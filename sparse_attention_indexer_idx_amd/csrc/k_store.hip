@@ -35,19 +35,67 @@ __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
 
 // Q preparation for the MXFP4 scorer: rotation of the leading 64 dims at the token's
 // position (the K store's rotation), MXFP4 packing, and the fold of the caller's factor
-// into the weights.  One wave per head vector; a position outside [0, max_pos) leaves
-// the vector unrotated.
+// into the weights.  Four head vectors per wave: a 16-lane group per vector, lane j of
+// the group holding dims 8j..8j+7 (one 16-byte load), so the NeoX partner of dim d < 32
+// (dim d + 32) sits in lane j ^ 4 of the same group and each 32-block is four lanes.
+// The arithmetic is the K store's (fp64, no fused operations; the block maximum does not
+// depend on its order), so the bytes equal the row routine's.  A position outside
+// [0, max_pos) leaves the vector unrotated.
+constexpr int kQVecsPerBlock = 16;
+
 __global__ __launch_bounds__(256) void q_prep_mxfp4_kernel(QPrepArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t v = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (v >= a.n_vecs) return;
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int64_t v_raw = (int64_t)blockIdx.x * kQVecsPerBlock + (threadIdx.x >> 4);
+  const bool live = v_raw < a.n_vecs;
+  const int64_t v = live ? v_raw : a.n_vecs - 1;  // lanes past the end compute a copy, store nothing
   const int32_t pos = a.positions[v / a.H];
-  const bool rot = pos >= 0 && pos < a.max_pos;  // wave-uniform
-  const uint16_t* x = a.q + v * 128;
-  const double y0 = bf16_to_f64(x[lane]), y1 = bf16_to_f64(x[lane + 64]);
-  const double z0 = rot ? rope_neox_lane(y0, lane, a.cos_sin + (int64_t)pos * 64) : y0;
-  pack_mxfp4_row(z0, y1, lane, (uint32_t*)(a.q_out + v * 64), (uint32_t*)(a.q_scale + v * 4), nullptr);
-  if (lane == 0) a.w_out[v] = (float)((double)a.w[v] * (double)a.w_scale);
+  const bool rot = pos >= 0 && pos < a.max_pos && j < 8;
+  const uint4 raw = *(const uint4*)(a.q + v * 128 + 8 * j);
+  const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+  double y[8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    y[2 * m] = bf16_to_f64((uint16_t)(wds[m] & 0xFFFFu));
+    y[2 * m + 1] = bf16_to_f64((uint16_t)(wds[m] >> 16));
+  }
+  const float* __restrict__ cs = a.cos_sin + (int64_t)(rot ? pos : 0) * 64;
+  double z[8];
+  double amax = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double partner = shfl_xor(y[e], 4);
+    const int i = 8 * (j & 3) + e;
+    const double c = (double)cs[i], n = (double)cs[32 + i];
+    double zr;
+    if (j < 4) {
+      const double ac = y[e] * c, bn = partner * n;
+      zr = ac - bn;
+    } else {
+      const double bc = y[e] * c, an = partner * n;
+      zr = bc + an;
+    }
+    z[e] = rot ? zr : y[e];
+    amax = fmax(amax, fabs(z[e]));
+  }
+  amax = fmax(amax, shfl_xor(amax, 1));
+  amax = fmax(amax, shfl_xor(amax, 2));
+  const int X = mx_block_exponent(amax);
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) word |= mxfp4_code(z[e], X) << (4 * e);
+  // scale bytes of blocks 0..3 from lanes 0, 4, 8, 12 of the group
+  const uint32_t sb = (uint32_t)(X + 127);
+  const int g0 = lane & 48;
+  const uint32_t sw = __shfl(sb, g0, 64) | (__shfl(sb, g0 + 4, 64) << 8) | (__shfl(sb, g0 + 8, 64) << 16) |
+                      (__shfl(sb, g0 + 12, 64) << 24);
+  if (live) {
+    reinterpret_cast<uint32_t*>(a.q_out + v * 64)[j] = word;
+    if (j == 0) {
+      *reinterpret_cast<uint32_t*>(a.q_scale + v * 4) = sw;
+      a.w_out[v] = (float)((double)a.w[v] * (double)a.w_scale);
+    }
+  }
 }
 
 // MXFP4 packing of head vectors: one thread per 32-element block.
@@ -119,7 +167,7 @@ hipError_t launch_k_store(const KStoreArgs& a, hipStream_t s) {
 
 hipError_t launch_q_prep_mxfp4(const QPrepArgs& a, hipStream_t s) {
   if (a.n_vecs == 0) return hipSuccess;
-  const int64_t blocks = (a.n_vecs + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t blocks = (a.n_vecs + kQVecsPerBlock - 1) / kQVecsPerBlock;
   hipLaunchKernelGGL(q_prep_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -172,6 +172,7 @@ def test_q_prep_checks(lib):
     assert f(pos=None) == bd.IDX_EINVAL
     assert f(qs=FAKE + 2) == bd.IDX_EALIGN
     assert f(qp=FAKE + 1) == bd.IDX_EALIGN
+    assert f(q=FAKE + 8) == bd.IDX_EALIGN   # the bf16 input is read 16 bytes per lane
     if no_gpu(lib):
         assert f() == bd.IDX_EUNSUPPORTED
 
