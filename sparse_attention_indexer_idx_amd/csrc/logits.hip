@@ -31,13 +31,18 @@ namespace {
 // ------------------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4;
 
-template <int FMT, int NT, int G>
+template <int FMT, int NT, int G, bool EXIT_DEAD = false>
 __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const int tok0 = (blockIdx.x * kDecodeWaves + wave) * (64 * G);
   NoPatch none;
-  decode_wave<FMT, NT, G>(a, blockIdx.y, tok0, threadIdx.x & 63, none);
+  decode_wave<FMT, NT, G, NoPatch, EXIT_DEAD>(a, blockIdx.y, tok0, threadIdx.x & 63, none);
 }
+
+// Calls this large run many rounds of waves, and with mixed context lengths many of them
+// lie wholly past their sequence: those leave before their K loads.  (Below it, the later
+// Q loads the early exit brings cost more than the dead waves do.)
+constexpr int64_t kExitDeadTokens = int64_t(1) << 21;
 
 // Row-split decode kernel for several query rows with many heads (e.g. 3 speculative
 // tokens x 64 heads): each wave holds one query row's head tiles instead of all rows', so
@@ -173,6 +178,15 @@ template <int FMT, int G>
 hipError_t launch_decode_g(const LogitsArgs& a, int nt, hipStream_t s) {
   const int tok_per_block = kDecodeWaves * 64 * G;
   const dim3 grid((unsigned)((a.max_ctx + tok_per_block - 1) / tok_per_block), (unsigned)a.B);
+  if (G == 2 && (int64_t)a.B * a.max_ctx >= kExitDeadTokens) {
+    switch (nt) {
+#define IDX_DECODE_EXIT_CASE(N) \
+  case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N, G, true>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      IDX_DECODE_EXIT_CASE(1) IDX_DECODE_EXIT_CASE(2) IDX_DECODE_EXIT_CASE(3) IDX_DECODE_EXIT_CASE(4)
+#undef IDX_DECODE_EXIT_CASE
+      default: break;
+    }
+  }
   switch (nt) {
 #define IDX_DECODE_CASE(N) \
   case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N, G>), grid, dim3(256), 0, s, a); break;
