@@ -172,7 +172,7 @@ int idx_q_prep_mxfp4(const void* q_bf16, int64_t n_tokens, int32_t H, const int3
  *      turns by (cos_sin[pos][i], cos_sin[pos][32+i]): a' = a c - b n, b' = b c + a n;
  *   a token whose slot is negative (padding), outside the pool, or whose position is
  *      outside [0, max_pos) is skipped: no K is stored, its q_fp8 bytes and w_out are 0.
- * pool: FP8 (IDX_EINVAL otherwise).  q_bf16 device bf16 [n_tokens][H][128]; k_bf16 device
+ * pool: FP8 (IDX_EINVAL otherwise).  q_bf16 device bf16 [n_tokens][H][128], 16-byte aligned; k_bf16 device
  * bf16 [n_tokens][128]; w, w_out device fp32 [n_tokens][H] (w_out may alias w);
  * positions int32 [n_tokens]; cos_sin fp32 [max_pos][64]; ln_gamma, ln_beta fp32 [128];
  * eps > 0; slot_mapping int64 [n_tokens]; q_fp8 device uint8 [n_tokens][H][128], 4-byte

@@ -143,7 +143,8 @@ IDX_EXPORT int idx_qk_prep_fp8(const idx_pool* pool, const void* q_bf16, const v
     return IDX_EINVAL;
   // one wave per vector: the grid's work-items (64 per vector) must fit in 32 bits
   if (n_tokens > (int64_t)(UINT32_MAX / 64) / (H + 1)) return IDX_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(q_fp8) & 3u) != 0) return IDX_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(q_fp8) & 3u) != 0 || (reinterpret_cast<uintptr_t>(q_bf16) & 15u) != 0)
+    return IDX_EALIGN;
   if ((st = check_device()) != IDX_OK) return st;
   idx::QKPrepArgs a;
   a.pool = view_of(pool);

@@ -222,6 +222,7 @@ def qk_prep_call(lib, p=None, **kw):
     (dict(max_pos=0), bd.IDX_EINVAL),
     (dict(k=None), bd.IDX_EINVAL),
     (dict(q8=FAKE + 2), bd.IDX_EALIGN),
+    (dict(q=FAKE + 8), bd.IDX_EALIGN),               # the bf16 queries are read 16 bytes per lane
     (dict(T=(1 << 26) // 9 + 1), bd.IDX_EINVAL),   # the grid would pass 2^32 work-items
 ])
 def test_qk_prep_checks(lib, kw, want):
