@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--kv", default="mxfp4", choices=["mxfp4", "fp8"])
     ap.add_argument("--warm", action="store_true", help="one pool replica (cache-resident)")
+    ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (decode workloads)")
     ap.add_argument("--eager", action="store_true",
                     help="report the eager step time as the value (default: HIP-graph replay of the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,7 +280,7 @@ def main():
     if bd.idx_device_check() != bd.IDX_OK:
         raise SystemExit("device is not gfx950")
     fmt = 0 if args.kv == "mxfp4" else 1
-    W = wl.make_workload(args.config, kv_format=fmt)
+    W = wl.make_workload(args.config, kv_format=fmt, scale={"H": args.heads} if args.heads else None)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
     P = W.page_size
     page_bytes = (68 if fmt == 0 else 132) * P
@@ -349,15 +350,18 @@ def main():
         bd.idx_decode_step(pools[i % replicas][1], k_new, gamma, W.eps, pos_new, cos_sin, slot_new, q, qs, w, pt, ctx,
                            W.B, W.n_q, W.H, W.max_ctx, logits, W.topk, out, ws)
 
+    # the step through idx_decode_step when it runs as the one fused kernel there
     fused = not args.separate and len(new) == W.B * W.n_q
     if fused:
         try:
-            fused_step(0)
-            torch.cuda.synchronize()
+            fused = bd.idx_decode_step_fused(W.B, W.n_q, W.H, W.max_ctx) == 1
         except bd.IdxError as e:
             if e.status != bd.IDX_EUNSUPPORTED:
                 raise
             fused = False
+    if fused:
+        fused_step(0)
+        torch.cuda.synchronize()
 
     def held(fn, n, host_s):
         """GPU time of n back-to-back calls fn(0..n-1): a spin kernel holds the GPU while

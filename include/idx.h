@@ -308,12 +308,13 @@ int idx_topk_candidates(const float* logits, int64_t logits_stride, const int32_
  * workspace        device memory of at least idx_decode_step_workspace_bytes(B) bytes,
  *                  4-byte aligned, zero-filled before its first use; every call leaves
  *                  it zero again.  Calls that share a workspace must not overlap.
- * Supported shapes (else IDX_EUNSUPPORTED, before anything is enqueued): n_q * ceil(H/16)
- * <= 2 and max_ctx <= 16384.
- * Execution: one kernel of 1024-thread blocks, each scoring 2048 tokens of a sequence;
- * when that grid (ceil(max_ctx / 2048) * B blocks) exceeds the device's CU count, the
- * K store, scorer and top-k kernels run one after another instead, with the same
- * results (the fused launch pays off only while every block has a CU to itself).
+ * Supported shapes (else IDX_EUNSUPPORTED, before anything is enqueued): the scorer's
+ * decode form, n_q * ceil(H/16) <= 16, and max_ctx <= 65536.
+ * Execution: one kernel of 1024-thread blocks, each scoring 2048 tokens of a sequence,
+ * when n_q * ceil(H/16) <= 2, max_ctx <= 16384 and that grid (ceil(max_ctx / 2048) * B
+ * blocks) fits the device's CU count; otherwise the K store, scorer and top-k kernels run
+ * one after another, with the same results (the fused launch pays off only while every
+ * block has a CU to itself and its registers hold the query tiles).
  * ------------------------------------------------------------------------------- */
 int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
                     float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
@@ -321,6 +322,12 @@ int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride
                     const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
                     int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
                     int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* How idx_decode_step runs this shape on the current device: 1 = the one fused kernel,
+ * 0 = the K store, scorer and top-k kernels in sequence; IDX_EUNSUPPORTED for a shape it
+ * does not take (or no gfx950 device), IDX_EINVAL for B, n_q or H below 1 or max_ctx < 0.
+ * Host-only; for callers and benchmarks that report which kernels ran. */
+int idx_decode_step_fused(int32_t B, int32_t n_q, int32_t H, int32_t max_ctx);
 
 /* Workspace bytes idx_decode_step needs for B sequences (a multiple of 256; 0 if B < 1). */
 size_t idx_decode_step_workspace_bytes(int32_t B);

@@ -19,7 +19,7 @@ IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_qk_prep_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
            "idx_logits_paged", "idx_logits_candidates", "idx_topk_candidates",
-           "idx_topk", "idx_decode_step", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_diag_mfma",
+           "idx_topk", "idx_decode_step", "idx_decode_step_fused", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_diag_mfma",
            "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
 
 
@@ -63,6 +63,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
         "idx_logits_candidates": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, V, I32, V, I64, V],
         "idx_topk_candidates": [V, I64, V, I32, I32, I32, I32, I32, V, V],
+        "idx_decode_step_fused": [I32, I32, I32, I32],
         "idx_decode_step": [PP, V, I64, V, F32, V, V, I32, V, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, I32,
                             V, V, ctypes.c_size_t, V],
         "idx_decode_step_workspace_bytes": [I32],
@@ -179,6 +180,14 @@ def idx_topk_candidates(logits, cand_blocks, page_size: int, B: int, n_q: int, k
 def idx_topk(logits, ctx_lens, B: int, n_q: int, max_ctx: int, k: int, out_idx, stream=None):
     _check("idx_topk", load().idx_topk(_ptr(logits), logits.stride(0), _ptr(ctx_lens), B, n_q, max_ctx, k,
                                        _ptr(out_idx), _stream(stream)))
+
+
+def idx_decode_step_fused(B: int, n_q: int, H: int, max_ctx: int) -> int:
+    """1 if idx_decode_step runs this shape as the one fused kernel, 0 if as three kernels."""
+    r = int(load().idx_decode_step_fused(B, n_q, H, max_ctx))
+    if r < 0:
+        _check("idx_decode_step_fused", r)
+    return r
 
 
 def idx_decode_step_workspace_bytes(B: int) -> int:

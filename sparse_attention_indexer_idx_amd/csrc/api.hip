@@ -334,6 +334,14 @@ IDX_EXPORT int idx_topk_candidates(const float* logits, int64_t logits_stride, c
   return hip_status(idx::launch_topk_candidates(a, static_cast<hipStream_t>(stream)));
 }
 
+IDX_EXPORT int idx_decode_step_fused(int32_t B, int32_t n_q, int32_t H, int32_t max_ctx) {
+  if (B < 1 || n_q < 1 || H < 1 || max_ctx < 0) return IDX_EINVAL;
+  if (H > idx::kMaxHeads || !idx::decode_step_supported(n_q, H, max_ctx)) return IDX_EUNSUPPORTED;
+  const int st = check_device();
+  if (st != IDX_OK) return st;
+  return idx::decode_step_fuses(B, n_q, H, max_ctx, num_cus()) ? 1 : 0;
+}
+
 IDX_EXPORT size_t idx_decode_step_workspace_bytes(int32_t B) {
   if (B < 1) return 0;
   return ((size_t)B * sizeof(int32_t) + 255) / 256 * 256;

@@ -23,7 +23,10 @@ namespace {
 constexpr int kStepWaves = 16;  // 1024-thread blocks: the last one runs a 1024-thread top-k
 constexpr int kStepG = 2;       // 128 tokens per wave
 constexpr int kStepTok = kStepWaves * 64 * kStepG;
-constexpr int kStepMaxTiles = 2;  // query head tiles per sequence (register budget of 1024-thread blocks)
+// Query head tiles per sequence the fused kernel takes: within the register budget of
+// 1024-thread blocks (128 VGPRs).  Four tiles fit MXFP4 with a few spills but ran the step
+// 1.5x slower than the three kernels (64 heads, B16/8K), so wider shapes take those.
+constexpr int kStepMaxTiles = 2;
 constexpr int kStepMaxCtx = 16 * 1024;
 constexpr int kRowWords = 33;   // one K row in page layout: 16 (or 32) data words, then the scale word
 
@@ -33,7 +36,7 @@ constexpr int kRowWords = 33;   // one K row in page layout: 16 (or 32) data wor
 // the first to finish scoring — then computes each such row after its own work (its K
 // tiles are no longer live, so the fp64 work has registers to spare), stores it to its
 // slot, leaves it in its LDS buffer, and rescores the token from it.
-template <int FMT>
+template <int FMT, int NQ>  // NQ >= n_q (the launch's head-tile count bounds it)
 struct NewRows {
   static constexpr bool kCoherentStores = true;
   static constexpr bool kNewRows = true;
@@ -42,12 +45,12 @@ struct NewRows {
   int blk0;        // first token of the block
   bool wave0;
   uint32_t* buf;   // wave 0's LDS row buffer (kRowWords words)
-  int s_new[kStepMaxTiles];  // new tokens of the block with a row to store, else -1
+  int s_new[NQ];  // new tokens of the block with a row to store, else -1
 
   __device__ __forceinline__ void prepare(int n_b) {
     const int n_q = a->s.n_q;
 #pragma unroll
-    for (int jn = 0; jn < kStepMaxTiles; ++jn) {
+    for (int jn = 0; jn < NQ; ++jn) {
       s_new[jn] = -1;
       if (jn >= n_q) continue;
       const int s = n_b - n_q + jn;
@@ -64,7 +67,7 @@ struct NewRows {
   __device__ __forceinline__ bool skip(int s) const {
     bool k = false;
 #pragma unroll
-    for (int jn = 0; jn < kStepMaxTiles; ++jn) k = k || s == s_new[jn];
+    for (int jn = 0; jn < NQ; ++jn) k = k || s == s_new[jn];
     return k;
   }
 
@@ -72,7 +75,7 @@ struct NewRows {
 
   template <int F>
   __device__ __forceinline__ bool new_row(int jn, int lane, KTile<F>& nk, int& s, int& slot4) const {
-    if (jn >= kStepMaxTiles || s_new[jn] < 0) return false;
+    if (jn >= NQ || s_new[jn] < 0) return false;
     s = s_new[jn];
     const int64_t i = (int64_t)b * a->s.n_q + jn;
     const int32_t pos = a->positions[i];
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
   const int b = blockIdx.y;
   const int blk0 = blockIdx.x * kStepTok;
   const int tok0 = blk0 + wave * (64 * kStepG);
-  NewRows<FMT> nr{&a, b, blk0, wave == 0, row_buf, {}};
+  NewRows<FMT, NT> nr{&a, b, blk0, wave == 0, row_buf, {}};
   decode_wave<FMT, NT, kStepG>(a.s, b, tok0, lane, nr);
 
   // Publish this block's logits and count it in.  The logits stores are device-coherent
@@ -155,14 +158,22 @@ hipError_t launch_fmt(const StepArgs& a, dim3 grid, int nt, int ept, hipStream_t
 }  // namespace
 
 bool decode_step_supported(int n_q, int H, int64_t max_ctx) {
-  return n_q >= 1 && n_q * ((H + kHeadTile - 1) / kHeadTile) <= kStepMaxTiles && max_ctx <= kStepMaxCtx;
+  return n_q >= 1 && logits_uses_decode_kernel(n_q, H) && max_ctx <= kTopkMaxCtx;
+}
+
+bool decode_step_fuses(int B, int n_q, int H, int max_ctx, int num_cus) {
+  const int64_t blocks = (int64_t)((max_ctx + kStepTok - 1) / kStepTok) * B;
+  const int nt = n_q * ((H + kHeadTile - 1) / kHeadTile);
+  return max_ctx > 0 && blocks <= num_cus && nt <= kStepMaxTiles && max_ctx <= kStepMaxCtx;
 }
 
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus) {
   const dim3 grid((unsigned)((a.s.max_ctx + kStepTok - 1) / kStepTok), (unsigned)a.s.B);
-  if (a.s.max_ctx == 0 || (int64_t)grid.x * grid.y > num_cus) {
-    // More blocks than CUs: a 1024-thread block per CU leaves the scorer short of waves
-    // in flight, so the three kernels run one after another instead (same bytes, same
+  const int nt = a.s.n_q * ((a.s.H + kHeadTile - 1) / kHeadTile);
+  if (!decode_step_fuses(a.s.B, a.s.n_q, a.s.H, a.s.max_ctx, num_cus)) {
+    // More blocks than CUs (a 1024-thread block per CU leaves the scorer short of waves in
+    // flight), more query head tiles than the fused kernel holds, or rows longer than its
+    // top-k takes: the three kernels run one after another instead (same bytes, same
     // bits: the same wave bodies and row routines).  With max_ctx == 0 every row is
     // empty and only the top-k (all -1) has work.
     KStoreArgs k;
@@ -187,7 +198,6 @@ hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus) {
     TopkArgs t{a.s.logits, a.s.lstride, a.s.ctx, a.s.B, a.s.n_q, a.s.max_ctx, a.k_top, a.out};
     return launch_topk(t, s);
   }
-  const int nt = a.s.n_q * ((a.s.H + kHeadTile - 1) / kHeadTile);
   int ept = 1;
   while (ept * 1024 < a.s.max_ctx) ept *= 2;
   return a.s.pool.kv_format == 0 ? launch_fmt<0>(a, grid, nt, ept, s) : launch_fmt<1>(a, grid, nt, ept, s);

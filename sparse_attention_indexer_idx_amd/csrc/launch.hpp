@@ -145,9 +145,12 @@ struct StepArgs {
   int32_t* out;
   int32_t* counters;  // [B] block counters: zero on entry, left zero on exit
 };
-// Whether the fused step takes this shape (n_q * ceil(H/16) <= 2 query head tiles per
-// sequence, rows of at most 16384 tokens).
+// Whether the decode step takes this shape: the scorer's decode form (n_q * ceil(H/16) <=
+// 16 query head tiles per sequence) and rows the top-k takes (max_ctx <= 65536).  It runs
+// fused for up to 2 head tiles and rows of up to 16384 tokens, else as three kernels.
 bool decode_step_supported(int n_q, int H, int64_t max_ctx);
+// Whether a supported step runs as the one fused kernel (else as three kernels).
+bool decode_step_fuses(int B, int n_q, int H, int max_ctx, int num_cus);
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus);
 // 8 * rounds MFMAs (16x16x128, fmt 0: E2M1 x E2M1, 1: e4m3 x e4m3) per wave on register
 // operands; out gets blocks * 256 floats.

@@ -172,8 +172,9 @@ CONFIG_NAMES = {
 
 def make_workload(config: int, kv_format: int = MXFP4, seed: int | None = None, *, gamma_random: bool = False,
                   scale: dict | None = None) -> Workload:
-    """Build one of the five workloads.  `scale` may override B/ctx for reduced test
-    variants (e.g. {"B": 4}); the default is the full shape."""
+    """Build one of the five workloads.  `scale` may override B/ctx, and for the decode
+    workloads the head count H and query tokens n_q, for test variants (e.g. {"B": 4});
+    the default is the full shape."""
     seed = 1000 + config if seed is None else seed
     ss = np.random.SeedSequence(seed)
     r_k, r_q, r_w, r_len, r_pg, r_misc = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(6)]
@@ -212,6 +213,11 @@ def make_workload(config: int, kv_format: int = MXFP4, seed: int | None = None, 
         w_div = np.sqrt(H)
     else:
         raise ValueError(f"unknown config {config}")
+    if "H" in scale:
+        H = int(scale["H"])
+        w_div = np.sqrt(H)
+    if "n_q" in scale and config != 2:
+        n_q = int(scale["n_q"])
     if "B" in scale:
         B = int(scale["B"])
         ctx = ctx[:B]

@@ -142,6 +142,15 @@ def step_call(lib, p=None, **kw):
                                d["ws"], ctypes.c_size_t(d["wsb"]), None)
 
 
+def test_decode_step_fused_query(lib):
+    assert lib.idx_decode_step_fused(0, 1, 32, 8192) == bd.IDX_EINVAL
+    assert lib.idx_decode_step_fused(64, 1, 32, -1) == bd.IDX_EINVAL
+    assert lib.idx_decode_step_fused(64, 5, 64, 8192) == bd.IDX_EUNSUPPORTED   # prefill form
+    assert lib.idx_decode_step_fused(64, 1, 32, 65537) == bd.IDX_EUNSUPPORTED
+    if no_gpu(lib):
+        assert lib.idx_decode_step_fused(64, 1, 32, 8192) == bd.IDX_EUNSUPPORTED
+
+
 def test_decode_step_checks(lib):
     assert lib.idx_decode_step_workspace_bytes(0) == 0
     assert lib.idx_decode_step_workspace_bytes(1) == 256 and lib.idx_decode_step_workspace_bytes(65) == 512
@@ -152,12 +161,14 @@ def test_decode_step_checks(lib):
     assert step_call(lib, rs=64) == bd.IDX_EINVAL
     assert step_call(lib, kk=0) == bd.IDX_EINVAL
     assert step_call(lib, D=64) == bd.IDX_EUNSUPPORTED
-    assert step_call(lib, H=48) == bd.IDX_EUNSUPPORTED                   # 3 head tiles
-    assert step_call(lib, n_q=2, wsb=lib.idx_decode_step_workspace_bytes(2)) == bd.IDX_EUNSUPPORTED  # 4 tiles
-    assert step_call(lib, mc=16385, mpp=1 << 10, ls=1 << 15) == bd.IDX_EUNSUPPORTED
+    assert step_call(lib, n_q=5, H=64) == bd.IDX_EUNSUPPORTED            # 20 head tiles: not the decode form
+    assert step_call(lib, mc=65537, mpp=1 << 11, ls=1 << 17) == bd.IDX_EUNSUPPORTED  # rows past the top-k's
     assert step_call(lib, mc=257) == bd.IDX_EINVAL                       # beyond the page table
     if no_gpu(lib):
         assert step_call(lib) == bd.IDX_EUNSUPPORTED
+        # wider shapes pass validation (and run as three kernels on a device)
+        assert step_call(lib, H=48) == bd.IDX_EUNSUPPORTED
+        assert step_call(lib, mc=16385, mpp=1 << 10, ls=1 << 15) == bd.IDX_EUNSUPPORTED
 
 
 def test_q_prep_checks(lib):

@@ -145,6 +145,53 @@ def test_step_large_pool(fmt):
     G.assert_topk_valid(out[rows], ref, W, rows, W.topk, 1e-4 * stats["max_abs_ref"], f"cfg4/fmt{fmt}")
 
 
+@pytest.mark.parametrize("cfg,fmt,scale", [
+    (1, wl.MXFP4, {"B": 16, "H": 64}),            # 64 heads of one query token: four head tiles
+    (1, wl.FP8, {"B": 6, "H": 64}),
+    (3, wl.MXFP4, {"B": 8, "H": 16}),             # three query tokens of 16 heads, page 64, offset pool
+    (3, wl.MXFP4, {"B": 10}),                     # three query tokens of 64 heads: the row-split scorer
+    (1, wl.MXFP4, {"B": 12, "H": 32, "n_q": 2}),  # two query tokens of 32 heads
+])
+def test_step_more_head_tiles(cfg, fmt, scale):
+    """Shapes with more query head tiles than the fused kernel holds run as the three
+    kernels inside the entry point: the same bytes and bits as the separate calls, and
+    the oracle within the tolerances."""
+    W = wl.make_workload(cfg, kv_format=fmt, scale=scale)
+    G.say(f"decode step cfg={cfg} fmt={fmt} {scale} (n_q={W.n_q}, H={W.H})")
+    b, lb, ob = compare_paths(W, fmt, label=f"cfg{cfg}/{scale}")
+    rows = np.arange(W.rows)
+    hp = G.CompactHostPool(W, fmt)
+    ref = G.oracle_logits(hp, b.q, b.qs, b.w, rows, W.max_ctx)
+    mask = G.valid_mask(W, rows, W.max_ctx)
+    stats = G.assert_logits_close(lb, ref, mask, f"cfg{cfg}/{scale}")
+    G.assert_topk_valid(ob, ref, W, rows, W.topk, 1e-4 * stats["max_abs_ref"], f"cfg{cfg}/{scale}")
+
+
+def test_step_fused_query():
+    """Which shapes run as the one fused kernel (on a device with at least 256 CUs)."""
+    assert bd.idx_decode_step_fused(64, 1, 32, 8192) == 1      # decode B64/H32/8K: 256 blocks
+    assert bd.idx_decode_step_fused(2, 1, 4, 256) == 1
+    assert bd.idx_decode_step_fused(256, 1, 32, 16384) == 0    # more blocks than CUs
+    assert bd.idx_decode_step_fused(16, 1, 64, 8192) == 0      # four head tiles
+    assert bd.idx_decode_step_fused(4, 1, 32, 20000) == 0      # rows past the fused top-k's
+    assert bd.idx_decode_step_fused(4, 1, 32, 0) == 0
+
+
+def test_step_rejects_prefill_shapes():
+    """More than 16 query head tiles per sequence is the scorer's prefill form, which the
+    decode step does not take: IDX_EUNSUPPORTED before anything is enqueued."""
+    W = wl.make_workload(1, scale={"B": 2, "H": 64, "n_q": 5, "ctx": 512})
+    ctx = np.asarray(W.ctx, np.int32)
+    new = new_rows(W, ctx)
+    old = np.setdiff1d(np.arange(W.k_rows.shape[0]), new[new >= 0])
+    st = Step(W, wl.MXFP4, ctx, G.CompactHostPool(W, wl.MXFP4, rows=old))
+    logits, out = st.buffers()
+    with pytest.raises(bd.IdxError) as e:
+        bd.idx_decode_step(st.pool.view, st.k_d, st.gamma_d, W.eps, st.pos_d, st.cs_d, st.slot_d, st.q_d, st.qs_d,
+                           st.w_d, st.pt_d, st.ctx_d, W.B, W.n_q, W.H, W.max_ctx, logits, W.topk, out, st.ws)
+    assert e.value.status == bd.IDX_EUNSUPPORTED
+
+
 def test_step_edges():
     """A padding slot (the row is neither stored nor substituted), an empty sequence and
     a sequence of one token, a context that is not a multiple of the block's tokens."""
