@@ -119,7 +119,7 @@ def traffic_from_profiles(kernel_key, src_hash):
     return None
 
 
-SCORER_SOURCES = ("logits.hip", "scorer.hpp", "device_common.hpp", "launch.hpp")
+SCORER_SOURCES = ("logits.hip", "logits_stream.hip", "scorer.hpp", "device_common.hpp", "launch.hpp")
 
 
 def scorer_source_hash():

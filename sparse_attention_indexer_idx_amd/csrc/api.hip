@@ -263,7 +263,7 @@ IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const ui
                        logits_stride, a);
   if (st != IDX_OK) return st;
   if ((st = check_device()) != IDX_OK) return st;
-  return hip_status(idx::launch_logits(a, static_cast<hipStream_t>(stream)));
+  return hip_status(idx::launch_logits(a, static_cast<hipStream_t>(stream), num_cus()));
 }
 
 IDX_EXPORT int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens, int32_t B, int32_t n_q,

@@ -193,7 +193,7 @@ hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus) {
     hipError_t e;
     if (a.s.max_ctx > 0) {
       if ((e = launch_k_store(k, s)) != hipSuccess) return e;
-      if ((e = launch_logits(a.s, s)) != hipSuccess) return e;
+      if ((e = launch_logits(a.s, s, num_cus)) != hipSuccess) return e;
     }
     TopkArgs t{a.s.logits, a.s.lstride, a.s.ctx, a.s.B, a.s.n_q, a.s.max_ctx, a.k_top, a.out};
     return launch_topk(t, s);

@@ -99,7 +99,10 @@ hipError_t launch_q_prep_mxfp4(const QPrepArgs& a, hipStream_t s);
 hipError_t launch_q_quant_mxfp4(const uint16_t* q, int64_t n_vecs, uint8_t* qp, uint8_t* qs, hipStream_t s);
 hipError_t launch_q_quant_fp8(const uint16_t* q, const float* w, int64_t n_vecs, uint8_t* q8, float* wo,
                               hipStream_t s);
-hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t s, int num_cus = 256);
+// Streaming decode scorer: one query row per wave over a strided set of 64-token chunks,
+// the next chunk's K in flight while the current one is scored (n_q <= 4).
+hipError_t launch_logits_stream(const LogitsArgs& a, int num_cus, hipStream_t s);
 // Whether the scorer takes its decode form (all query rows of a sequence in registers).
 bool logits_uses_decode_kernel(int n_q, int H);
 // Largest max_ctx the scorer accepts for this shape (the prefill form splits the context

@@ -284,10 +284,12 @@ int64_t logits_max_ctx(int n_q, int H, int page_size) {
   return (int64_t)kMaxChunks * std::min(64 * page_size, 1 << 30);
 }
 
-hipError_t launch_logits(const LogitsArgs& args, hipStream_t s) {
+hipError_t launch_logits(const LogitsArgs& args, hipStream_t s, int num_cus) {
   if (args.max_ctx == 0) return hipSuccess;
   const LogitsArgs& a = args;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
+  // several query rows with many heads: the streaming row-split form
+  if (a.n_q > 1 && a.n_q <= 4 && a.n_q * ht > 4) return launch_logits_stream(a, num_cus, s);
   if (logits_uses_decode_kernel(a.n_q, a.H))
     return a.pool.kv_format == 0 ? launch_decode<0>(a, a.n_q * ht, s) : launch_decode<1>(a, a.n_q * ht, s);
   return a.pool.kv_format == 0 ? launch_prefill<0>(a, ht, s) : launch_prefill<1>(a, ht, s);
