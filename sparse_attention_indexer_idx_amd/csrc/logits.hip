@@ -31,18 +31,17 @@ namespace {
 // ------------------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4;
 
-template <int FMT, int NT, int G, bool EXIT_DEAD = false>
+template <int FMT, int NT, int G>
 __global__ __launch_bounds__(256) void logits_decode_kernel(LogitsArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const int tok0 = (blockIdx.x * kDecodeWaves + wave) * (64 * G);
   NoPatch none;
-  decode_wave<FMT, NT, G, NoPatch, EXIT_DEAD>(a, blockIdx.y, tok0, threadIdx.x & 63, none);
+  decode_wave<FMT, NT, G>(a, blockIdx.y, tok0, threadIdx.x & 63, none);
 }
 
-// Calls this large run many rounds of waves, and with mixed context lengths many of them
-// lie wholly past their sequence: those leave before their K loads.  (Below it, the later
-// Q loads the early exit brings cost more than the dead waves do.)
-constexpr int64_t kExitDeadTokens = int64_t(1) << 21;
+// Calls this large run many rounds of one-pass waves; the streaming form keeps the memory
+// system busy across them instead (and its waves stop at their sequence's end).
+constexpr int64_t kStreamTokens = int64_t(1) << 21;
 
 // Row-split decode kernel for several query rows with many heads (e.g. 3 speculative
 // tokens x 64 heads): each wave holds one query row's head tiles instead of all rows', so
@@ -178,15 +177,6 @@ template <int FMT, int G>
 hipError_t launch_decode_g(const LogitsArgs& a, int nt, hipStream_t s) {
   const int tok_per_block = kDecodeWaves * 64 * G;
   const dim3 grid((unsigned)((a.max_ctx + tok_per_block - 1) / tok_per_block), (unsigned)a.B);
-  if (G == 2 && (int64_t)a.B * a.max_ctx >= kExitDeadTokens) {
-    switch (nt) {
-#define IDX_DECODE_EXIT_CASE(N) \
-  case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N, G, true>), grid, dim3(256), 0, s, a); return hipGetLastError();
-      IDX_DECODE_EXIT_CASE(1) IDX_DECODE_EXIT_CASE(2) IDX_DECODE_EXIT_CASE(3) IDX_DECODE_EXIT_CASE(4)
-#undef IDX_DECODE_EXIT_CASE
-      default: break;
-    }
-  }
   switch (nt) {
 #define IDX_DECODE_CASE(N) \
   case N: hipLaunchKernelGGL((logits_decode_kernel<FMT, N, G>), grid, dim3(256), 0, s, a); break;
@@ -290,6 +280,10 @@ hipError_t launch_logits(const LogitsArgs& args, hipStream_t s, int num_cus) {
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
   // several query rows with many heads: the streaming row-split form
   if (a.n_q > 1 && a.n_q <= 4 && a.n_q * ht > 4) return launch_logits_stream(a, num_cus, s);
+  // one row per sequence over many tokens (mixed lengths likely): the streaming form too,
+  // with non-temporal K loads (measured: B256 with 4K-16K contexts 46.3 -> 41.7 us; on
+  // B64/8K the one-pass kernel stays faster, 8.5 vs 9.5 us)
+  if (a.n_q == 1 && (int64_t)a.B * a.max_ctx >= kStreamTokens) return launch_logits_stream(a, num_cus, s);
   if (logits_uses_decode_kernel(a.n_q, a.H))
     return a.pool.kv_format == 0 ? launch_decode<0>(a, a.n_q * ht, s) : launch_decode<1>(a, a.n_q * ht, s);
   return a.pool.kv_format == 0 ? launch_prefill<0>(a, ht, s) : launch_prefill<1>(a, ht, s);

@@ -18,7 +18,7 @@
 namespace idx {
 namespace {
 
-template <int FMT, int HT>
+template <int FMT, int HT, bool NT_LOADS>
 __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -60,11 +60,11 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
       if (FMT == 0) {
         // 16 bytes of the token's nibbles; its four E8M0 bytes as one word (the lane's own
         // byte is shifted down when the tile is scored, so no byte load waits in the loop)
-        const u32x4 x = *(const u32x4*)(page + (tok * 64u + 16u * g));
+        const u32x4 x = ld<NT_LOADS>((const u32x4*)(page + (tok * 64u + 16u * g)));
         K[t].v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        K[t].scale = *(const uint32_t*)(page + ((uint32_t)P * 64u + tok * 4u));
+        K[t].scale = ld<NT_LOADS>((const uint32_t*)(page + ((uint32_t)P * 64u + tok * 4u)));
       } else {
-        K[t] = load_k_tile<FMT, false>(page, P, use ? (s0 & (P - 1)) : 0, lane);
+        K[t] = load_k_tile<FMT, NT_LOADS>(page, P, use ? (s0 & (P - 1)) : 0, lane);
       }
       ok[t] = valid_page;
     }
@@ -109,7 +109,10 @@ template <int FMT>
 hipError_t launch_stream_fmt(const LogitsArgs& a, dim3 grid, int ht, hipStream_t s) {
   switch (ht) {
 #define IDX_STREAM_CASE(N) \
-  case N: hipLaunchKernelGGL((logits_stream_kernel<FMT, N>), grid, dim3(256), 0, s, a); break;
+  case N: \
+    if (a.n_q == 1) hipLaunchKernelGGL((logits_stream_kernel<FMT, N, true>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((logits_stream_kernel<FMT, N, false>), grid, dim3(256), 0, s, a); \
+    break;
     IDX_STREAM_CASE(1) IDX_STREAM_CASE(2) IDX_STREAM_CASE(3) IDX_STREAM_CASE(4)
     IDX_STREAM_CASE(5) IDX_STREAM_CASE(6) IDX_STREAM_CASE(7) IDX_STREAM_CASE(8)
 #undef IDX_STREAM_CASE

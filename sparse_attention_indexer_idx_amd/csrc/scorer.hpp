@@ -162,7 +162,7 @@ struct NoPatch {
 // j_base = 0 and NT = n_q * HT; one row when NT = HT).  EXIT_DEAD: a wave wholly past its
 // sequence leaves before its K loads (worth it where many waves are: many heads and mixed
 // lengths); the price is that the compiler then issues the Q loads after the page-table
-// round trip instead of before it.  STREAM_K: K loads are non-temporal (read once per
+// round trip instead of before it, so the single-row decode kernel does without.  STREAM_K: K loads are non-temporal (read once per
 // call); off where several waves read the same tiles from the cache.
 template <int FMT, int NT, int G, class Patch, bool EXIT_DEAD = false, bool STREAM_K = true>
 __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, Patch& patch,
