@@ -156,3 +156,20 @@ def test_scorer_deterministic():
     a = run_scorer(W, d).cpu().numpy()
     b = run_scorer(W, d).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("scale", [
+    {"B": 12, "n_q": 2, "H": 48},            # two rows per wave group: two chunk lanes per block
+    {"B": 8, "n_q": 4, "H": 32},             # four rows: one chunk lane, every wave a row
+    {"B": 9, "n_q": 3, "H": 64, "ctx": 300}, # short contexts: one or two chunks per row
+])
+@pytest.mark.parametrize("fmt", [wl.MXFP4, wl.FP8])
+def test_logits_streaming_shapes(scale, fmt):
+    """The streaming row-split scorer (2-4 query rows with more than four head tiles in all)
+    on mixed context lengths, page 64, an offset pool with gaps: every row against the
+    oracle, masked cells untouched."""
+    W = wl.make_workload(3, kv_format=fmt, scale=scale)
+    G.say(f"logits streaming form fmt={fmt} {scale}")
+    d = setup_scorer(W, fmt)
+    logits = run_scorer(W, d)
+    check(W, d, logits, np.arange(W.rows), f"stream {scale}/fmt{fmt}")
