@@ -278,7 +278,8 @@ int idx_logits_candidates(const idx_pool* pool, const uint8_t* q, const uint8_t*
  * holding -inf are not candidates; among the others, the k with the largest logits, as
  * token indices cand_blocks[r][c] * P + i.  A row with at most k candidate cells outputs
  * all of their tokens, then -1.  Equal logits go to the earlier cell (the smaller token
- * when a row's ids ascend); the order within a row is unspecified but deterministic.
+ * when a row's ids ascend); the order within a row is unspecified but deterministic.  NaN
+ * logits (a page id outside the pool) are outside the contract, as for idx_topk.
  * logits device fp32 [B * n_q][logits_stride]; cand_blocks device int32 [B * n_q][n_cand];
  * page_size P as the pool's; n_cand * P <= logits_stride and <= 65536; k >= 1;
  * out_idx device int32 [B * n_q][k]. */
