@@ -65,13 +65,12 @@ __global__ __launch_bounds__(256) void logits_decode_rows_kernel(LogitsArgs a) {
 // Prefill / long query sets: each wave owns 4 query rows (one per lane group after the
 // transpose-reduce) and walks 16-token K tiles; a block is 4 waves = 16 rows.  Work
 // units are (16-row block, token chunk) pairs enumerated chunk-major from a host-built
-// table so that no unit is empty and all units have similar cost.  The wave keeps the
-// physical ids of the next 64 logical pages one per lane.
+// table so that no unit is empty and all units have similar cost.  The waves keep the
+// physical ids of the unit's (at most 64) logical pages one per lane.
 // ------------------------------------------------------------------------------------
 constexpr int kPrefillRowsPerWave = 4;
 constexpr int kPrefillRowsPerBlock = 16;
 constexpr int kMaxChunks = 256;
-constexpr int kRing = 4;  // K tiles in flight per wave
 
 struct PrefillPlan {
   int32_t chunk;                      // tokens per chunk (multiple of 16)
@@ -81,12 +80,28 @@ struct PrefillPlan {
   int32_t qb_min[kMaxChunks];         // first row block that reaches each chunk
 };
 
+
+// Prefill form with the K tiles shared through LDS: the four waves of a block score the
+// same tokens for different rows, so each group of four 16-token tiles is fetched once
+// per block (wave w fetches tile w into registers, then LDS; lane l of every wave reads
+// back the operand lane l fetched, which is its own MFMA operand for that tile).  Two LDS
+// buffers alternate, with one barrier per group; the next group's fetch is in flight
+// while the current one is scored.  Block-uniform token range (the block's last row), so
+// every wave runs the same number of groups.
+constexpr int kStageTiles = 8;  // tiles per group: kStageTiles / 4 per wave
+
+template <int FMT>
+struct alignas(16) PrefillStage {
+  uint4 data[2][kStageTiles][64][FMT == 0 ? 1 : 2];
+  uint32_t scale[2][kStageTiles][64];
+};
+
 template <int FMT, int HT>
 __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, PrefillPlan plan) {
+  __shared__ PrefillStage<FMT> st;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int b = blockIdx.y;
-  // unit -> (chunk c, row block qb): binary search of the prefix table (scalar).
   const int u = blockIdx.x;
   int lo = 0, hi = plan.n_chunks - 1;
   while (lo < hi) {
@@ -94,81 +109,102 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
     if (plan.unit_start[mid] <= u) lo = mid; else hi = mid - 1;
   }
   const int c = lo;
-  const int qb = plan.n_qb - 1 - (u - plan.unit_start[c]);  // heaviest row blocks first
-  const int j0 = qb * kPrefillRowsPerBlock + wave * kPrefillRowsPerWave;
-  if (j0 >= a.n_q) return;
+  const int qb = plan.n_qb - 1 - (u - plan.unit_start[c]);
+  const int jb = qb * kPrefillRowsPerBlock;  // first row of the block
+  const int j0 = jb + wave * kPrefillRowsPerWave;
   const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
-  const int j_last = std::min(j0 + kPrefillRowsPerWave, a.n_q) - 1;
-  const int t_end = std::min(valid_len(n_b, a.n_q, j_last), (c + 1) * plan.chunk);
+  const int jb_last = std::min(jb + kPrefillRowsPerBlock, a.n_q) - 1;
+  const int t_end = std::min(valid_len(n_b, a.n_q, jb_last), (c + 1) * plan.chunk);  // block-uniform
   const int t_begin = c * plan.chunk;
-  if (t_begin >= t_end) return;
+  if (t_begin >= t_end) return;  // the whole block
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
   const int last_page = (t_end - 1) >> lgP;
-
-  // Page ids of the unit's pages, one per lane (a chunk spans at most 64 pages).
   const int page0 = t_begin >> lgP;
   const int32_t win = ptb[std::min(page0 + lane, last_page)];
-  auto tile_page = [&](int s0) -> const uint8_t* {  // s0 < t_end
-    const int32_t pid = __builtin_amdgcn_readlane(win, (s0 >> lgP) - page0);
-    const bool valid_page = pid >= 0 && (int64_t)pid < a.pool.num_pages;
-    return valid_page ? a.pool.base + (int64_t)pid * a.pool.stride : nullptr;
+  auto tile_ok = [&](int s0) {  // uniform
+    const int32_t pid = __builtin_amdgcn_readlane(win, (std::min(s0, t_end - 1) >> lgP) - page0);
+    return s0 < t_end && pid >= 0 && (int64_t)pid < a.pool.num_pages;
   };
 
   v8i qa[kPrefillRowsPerWave][HT];
   uint32_t qs[kPrefillRowsPerWave][HT];
   v4f qw[kPrefillRowsPerWave][HT];
-  int nv[kPrefillRowsPerWave];
 #pragma unroll
   for (int g = 0; g < kPrefillRowsPerWave; ++g) {
     const int j = std::min(j0 + g, a.n_q - 1);
     const int64_t r = (int64_t)b * a.n_q + j;
-    nv[g] = (j0 + g < a.n_q) ? valid_len(n_b, a.n_q, j0 + g) : 0;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       load_q_tile<FMT>(a, r, ht, lane, qa[g][ht], qs[g][ht]);
       qw[g][ht] = load_w_tile(a, r, ht, lane);
     }
   }
-  // the valid length this lane's output column belongs to after the transpose
-  const int my_n = nv[lane >> 4];
-  float* out_row = a.logits + ((int64_t)b * a.n_q + std::min(j0 + (lane >> 4), a.n_q - 1)) * a.lstride;
+  const int jr = j0 + (lane >> 4);
+  const int my_n = jr < a.n_q ? valid_len(n_b, a.n_q, jr) : 0;
+  float* out_row = a.logits + ((int64_t)b * a.n_q + std::min(jr, a.n_q - 1)) * a.lstride;
   const float qnan = __builtin_nanf("");
 
-  // A ring of kRing tiles in flight: slot i always holds tile base + 16*i of the current
-  // round; after slot i is consumed it is refilled with the same slot of the next round.
-  // The ring index is static (fully unrolled), so no register copy ever touches a tile
-  // whose load is still in flight.
-  KTile<FMT> ring[kRing];
-  bool rok[kRing];
-  auto fetch = [&](int s, KTile<FMT>& t, bool& okk) {
-    const uint8_t* pg = (s < t_end) ? tile_page(s) : nullptr;
-    okk = pg != nullptr;
-    t = load_k_tile<FMT, false>(pg ? pg : a.pool.base, P, pg ? (s & (P - 1)) : 0, lane);
+  constexpr int TPW = kStageTiles / 4;  // tiles each wave fetches per group
+  // tile w*TPW + i of group gg (tokens t_begin + 16*kStageTiles*gg + 16*(w*TPW + i))
+  auto fetch = [&](int gg, int i) {
+    const int s0 = t_begin + 16 * kStageTiles * gg + 16 * (wave * TPW + i);
+    const bool okk = tile_ok(s0);
+    const int32_t pid = __builtin_amdgcn_readlane(win, (std::min(s0, t_end - 1) >> lgP) - page0);
+    const uint8_t* page = a.pool.base + (okk ? (int64_t)pid : 0) * a.pool.stride;
+    return load_k_tile<FMT, false>(page, P, okk ? (s0 & (P - 1)) : 0, lane);
   };
+  auto stash = [&](int buf, int i, const KTile<FMT>& k) {
+    const int t = wave * TPW + i;
+    st.data[buf][t][lane][0] = make_uint4((uint32_t)k.v[0], (uint32_t)k.v[1], (uint32_t)k.v[2], (uint32_t)k.v[3]);
+    if (FMT == 1)
+      st.data[buf][t][lane][FMT] = make_uint4((uint32_t)k.v[4], (uint32_t)k.v[5], (uint32_t)k.v[6], (uint32_t)k.v[7]);
+    st.scale[buf][t][lane] = k.scale;
+  };
+  auto unstash = [&](int buf, int t) {
+    KTile<FMT> k;
+    const uint4 x = st.data[buf][t][lane][0];
+    if (FMT == 0) {
+      k.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+    } else {
+      const uint4 y = st.data[buf][t][lane][FMT];
+      k.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    }
+    k.scale = st.scale[buf][t][lane];
+    return k;
+  };
+
+  const int n_groups = (t_end - t_begin + 16 * kStageTiles - 1) / (16 * kStageTiles);
+  KTile<FMT> nxt[TPW];
 #pragma unroll
-  for (int i = 0; i < kRing; ++i) fetch(t_begin + 16 * i, ring[i], rok[i]);
-  for (int base = t_begin; base < t_end; base += 16 * kRing) {
+  for (int i = 0; i < TPW; ++i) nxt[i] = fetch(0, i);
+  for (int gg = 0; gg < n_groups; ++gg) {
+    const int buf = gg & 1;
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int s0 = base + 16 * i;
+    for (int i = 0; i < TPW; ++i) stash(buf, i, nxt[i]);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) nxt[i] = fetch(gg + 1, i);  // past the end: page 0 row 0, never stashed
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kStageTiles; ++t) {
+      const int s0 = t_begin + 16 * kStageTiles * gg + 16 * t;
       if (s0 < t_end) {  // uniform
+        const KTile<FMT> kt = unstash(buf, t);
         float p[kPrefillRowsPerWave];
 #pragma unroll
         for (int g = 0; g < kPrefillRowsPerWave; ++g) {
           float acc = 0.0f;
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc = relu_dot_acc(mfma<FMT>(qa[g][ht], qs[g][ht], ring[i]), qw[g][ht], acc,
-                                                              ht == 0);
+          for (int ht = 0; ht < HT; ++ht)
+            acc = relu_dot_acc(mfma<FMT>(qa[g][ht], qs[g][ht], kt), qw[g][ht], acc, ht == 0);
           p[g] = acc;
         }
         float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
-        if (FMT == 1) logit *= __uint_as_float(ring[i].scale);
-        if (!rok[i]) logit = qnan;
+        if (FMT == 1) logit *= __uint_as_float(kt.scale);
+        if (!tile_ok(s0)) logit = qnan;
         const int s = s0 + (lane & 15);
         if (s < my_n) out_row[s] = logit;
       }
-      fetch(s0 + 16 * kRing, ring[i], rok[i]);
     }
   }
 }
