@@ -122,9 +122,11 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
   const int last_page = (t_end - 1) >> lgP;
   const int page0 = t_begin >> lgP;
   const int32_t win = ptb[std::min(page0 + lane, last_page)];
+  // page ids are int32, so the bound fits one (a 32-bit compare stays on the scalar unit)
+  const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);
   auto tile_ok = [&](int s0) {  // uniform
     const int32_t pid = __builtin_amdgcn_readlane(win, (std::min(s0, t_end - 1) >> lgP) - page0);
-    return s0 < t_end && pid >= 0 && (int64_t)pid < a.pool.num_pages;
+    return s0 < t_end && pid >= 0 && pid < np32;
   };
 
   v8i qa[kPrefillRowsPerWave][HT];

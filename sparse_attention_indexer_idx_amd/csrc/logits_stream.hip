@@ -46,6 +46,7 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   const int n_ch = (n_r + 63) >> 6;
   if (c >= n_ch) return;  // uniform: nothing to score
 
+  const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);  // page ids are int32
   // Issue the four K tiles of chunk cc (any cc: past the row they read page 0 row 0).
   auto issue = [&](int cc, KTile<FMT>* K, bool* ok) {
     const bool live = cc < n_ch;
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
     for (int t = 0; t < 4; ++t) {
       const int s0 = 64 * cc + 16 * t;
       const int32_t pid = uniform(ptb[std::min(s0 >> lgP, last_page)]);
-      const bool valid_page = pid >= 0 && (int64_t)pid < a.pool.num_pages;
+      const bool valid_page = pid >= 0 && pid < np32;
       const bool use = live && valid_page;
       const uint8_t* page = a.pool.base + (use ? (int64_t)pid : 0) * a.pool.stride;
       const uint32_t tok = (uint32_t)((use ? (s0 & (P - 1)) : 0) + (lane & 15)), g = (uint32_t)(lane >> 4);
