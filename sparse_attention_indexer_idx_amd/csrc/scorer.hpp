@@ -202,10 +202,11 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
   // inside the pool); invalid pages score NaN below, dead waves store nothing.
   KTile<FMT> kt[T];
   bool ok[T];
+  const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);  // page ids are int32
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int s0 = tok0 + 16 * t;
-    const bool valid_page = pid[t] >= 0 && (int64_t)pid[t] < a.pool.num_pages;
+    const bool valid_page = pid[t] >= 0 && pid[t] < np32;
     const bool use = live && valid_page;
     const uint8_t* page = a.pool.base + (use ? (int64_t)pid[t] : 0) * a.pool.stride;
     kt[t] = load_k_tile<FMT, STREAM_K>(page, P, use ? (s0 & (P - 1)) : 0, lane);
@@ -267,7 +268,7 @@ __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0
         if (!patch.template new_row<FMT>(jn, lane, nk, s_new, slot4)) continue;
         // page validity of the token's tile, as its own wave sees it
         const int32_t pid_new = uniform(ptb[std::min(s_new >> lgP, last_page)]);
-        const bool okt = pid_new >= 0 && (int64_t)pid_new < a.pool.num_pages;
+        const bool okt = pid_new >= 0 && pid_new < np32;
         const KTile<FMT> k4[4] = {nk, nk, nk, nk};
         const bool ok4[4] = {okt, okt, okt, okt};
         const bool mine = lane == 16 * slot4 + (s_new & 15);
