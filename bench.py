@@ -553,17 +553,21 @@ def main():
     }
     result["device"] = device_rates(held, host_s)
     result["qk_prep_fp8_us"] = qk_prep_fp8_times(held, host_s, args.steps)
-    result["precision_vs_unquantized"] = precision_vs_unquantized(W, logits.cpu().numpy(), out.cpu().numpy())
     if not args.no_cpu_baseline:
+        # the CPU leg: the oracle timed on the host cores, and the same-run precision
+        # comparison against the oracle's unquantised scorer
         result["cpu_baseline"] = cpu_baseline(W, fmt, args.cpu_budget_s)
+        result["precision_vs_unquantized"] = precision_vs_unquantized(W, logits.cpu().numpy(), out.cpu().numpy())
     print(json.dumps(result), flush=True)
 
 
 def precision_vs_unquantized(W, logits, out, n_rows=4):
-    """This arm's logits and top-k against the method on unquantised operands: bf16 K rows
-    through RMSNorm and NeoX RoPE, bf16 Q, fp32 weights, all in fp64 (no MXFP4 / e4m3
-    rounding).  Cosine over the valid cells and top-k recall, on n_rows sampled rows with
-    more than k valid cells (the longest row of each sampled sequence)."""
+    """This arm's logits and top-k against the method on unquantised operands (bf16 K rows
+    through RMSNorm and NeoX RoPE, bf16 Q, fp32 weights, all fp64, with no MXFP4 or e4m3
+    rounding), computed by the oracle's unquantised K rows (oracle.k_rows_exact) and
+    scorer (oracle.logits_exact).  Cosine over the valid cells and top-k recall, on
+    n_rows sampled rows with more than k valid cells (part of the CPU leg)."""
+    import oracle
     from sparse_attention_indexer_idx_amd import workloads as wl
     cand = [r for r in range(W.rows) if W.valid_len(r) > W.topk]
     if not cand:
@@ -574,22 +578,18 @@ def precision_vs_unquantized(W, logits, out, n_rows=4):
     for r in rows:
         b, j = divmod(r, W.n_q)
         n = W.valid_len(r)
-        x = wl.bf16_bits_to_f32(W.k_rows[offs[b]: offs[b] + n]).astype(np.float64)
-        y = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + np.float64(W.eps)) * W.gamma.astype(np.float64)
-        cs = W.cos_sin[W.positions[offs[b]: offs[b] + n]].astype(np.float64)
-        c, sn = cs[:, :32], cs[:, 32:]
-        z = y.copy()
-        z[:, :32] = y[:, :32] * c - y[:, 32:64] * sn
-        z[:, 32:64] = y[:, 32:64] * c + y[:, :32] * sn
-        q = wl.bf16_bits_to_f32(W.q_rows[b, j]).astype(np.float64)          # [H, 128]
-        ref = np.maximum(z @ q.T, 0.0) @ W.w[b, j].astype(np.float64)       # [n]
+        z = oracle.k_rows_exact(W.k_rows[offs[b]: offs[b] + n], W.gamma, W.eps, W.positions[offs[b]: offs[b] + n],
+                                W.cos_sin)                                       # [n, 128]
+        q = wl.bf16_bits_to_f32(W.q_rows[b, j]).astype(np.float64)              # [H, 128]
+        ref = oracle.logits_exact(q.reshape(1, W.H, 128), W.w[b, j], z.reshape(1, n, 128), np.array([n], np.int32),
+                                  1, W.H, n, np.zeros(1, np.int64))[0]
         got = logits[r, :n].astype(np.float64)
         cos.append(float(got @ ref / (np.linalg.norm(got) * np.linalg.norm(ref))))
         top_ref = np.argsort(-ref, kind="stable")[:W.topk]
         rec.append(len(np.intersect1d(top_ref, out[r][out[r] >= 0])) / W.topk)
     return {"rows": rows, "cosine_min": round(min(cos), 7), "topk_recall_min": round(min(rec), 4),
             "topk_recall_mean": round(float(np.mean(rec)), 4),
-            "reference": "fp64 logits of the unquantised bf16 K (RMSNorm + NeoX RoPE) and Q"}
+            "reference": "the oracle's fp64 logits of the unquantised bf16 K (RMSNorm + NeoX RoPE) and Q"}
 
 
 def qk_prep_fp8_times(held, host_s, steps):

@@ -7,8 +7,8 @@
  * and formulas written out below, each taken from the pages that define the method:
  *
  *   [p1] "[ROCm][Perf] Add AITER paged MXFP4 sparse indexing on gfx950"
- *        (vllm PR 57517) — Purpose; Performance and accuracy (isolated scorer table);
- *        the statement that both MXFP4 kernels match the exact FP4-dequant reference.
+ *        (vllm PR 57517) — Purpose; Performance and accuracy (isolated scorer table
+ *        and its accuracy column).
  *   [p2] "Dense MXFP4 indexer for DeepSeek-V4 on ROCm" (vllm PR 60834) — Purpose
  *        (an MXFP4 indexer row is 68 B against FP8's 132 B; the MQA-logits kernel
  *        reads the cache in place; V4's packer uses cvt.rn.satfinite.e2m1x2);

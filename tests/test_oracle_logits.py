@@ -219,3 +219,91 @@ def test_fp8_logits_exact():
                 d *= Fraction(float(sks[t]))
                 tot += Fraction(float(w[0, r, h])) * max(d, Fraction(0))
             assert abs(Fraction(out[r, s]) - tot) <= Fraction(1, 10 ** 12) * (abs(tot) + 1)
+
+
+# ----------------------------------------------------------------------------------------
+# The unquantised scorer (oracle.logits_exact): the method on fp64 rows with no MXFP4 or
+# e4m3 rounding, used as the reference of the same-run precision comparison.
+
+def _dequant_mxfp4(nibble_bytes, scale_bytes):
+    """fp64 values of packed MXFP4 vectors from the spec table (independent of the oracle):
+    [..., 64] nibble bytes + [..., 4] E8M0 bytes -> [..., 128]."""
+    lut = np.array([float(v) for v in ind.E2M1_VALUES], np.float64)
+    nb = np.asarray(nibble_bytes, np.uint8)
+    codes = np.stack([nb & 15, nb >> 4], axis=-1).reshape(nb.shape[:-1] + (128,))
+    scale = np.ldexp(1.0, np.asarray(scale_bytes, np.int64) - 127)             # [..., 4]
+    return lut[codes] * np.repeat(scale, 32, axis=-1)
+
+
+def test_logits_exact_equals_paged_on_representable_rows():
+    """On rows that MXFP4 represents exactly, the unquantised scorer fed the dequantised
+    rows must give the packed scorer's logits bit for bit (every product and block sum is
+    exact in fp64, so no rounding order can separate them), masked cells included."""
+    rng = np.random.default_rng(27)
+    for (B, n_q, H, ctx, P) in ((2, 1, 4, [70, 33], 32), (1, 5, 3, [40], 16), (3, 2, 2, [16, 1, 50], 16)):
+        c = rand_mxfp4_case(rng, B=B, n_q=n_q, H=H, ctx=ctx, P=P)
+        S = int(c["ctx"].max())
+        k_rows = np.zeros((B, S, 128), np.float64)
+        for b in range(B):
+            for s in range(int(c["ctx"][b])):
+                base = c["offset"] + int(c["pt"][b, s // P]) * c["stride"]
+                row = s % P
+                k_rows[b, s] = _dequant_mxfp4(c["pool"][base + 64 * row: base + 64 * row + 64],
+                                              c["pool"][base + 64 * P + 4 * row: base + 64 * P + 4 * row + 4])
+        q_rows = _dequant_mxfp4(c["q"], c["qs"]).reshape(B * n_q, H, 128)
+        rows = np.arange(B * n_q, dtype=np.int64)
+        got = oracle.logits_exact(q_rows, c["w"].reshape(-1), k_rows, c["ctx"], n_q, H, S, rows)
+        want = run_oracle(c, out_stride=S)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_logits_exact_integer_brute_force():
+    """Small-integer rows and power-of-two weights keep every step exact; the expected
+    logits come from Python integers and Fractions cell by cell (the valid-length rule
+    included: masked cells are NaN)."""
+    rng = np.random.default_rng(28)
+    B, n_q, H, S = 2, 3, 5, 9
+    ctx = np.array([9, 4], np.int32)
+    q_rows = rng.integers(-3, 4, (B * n_q, H, 128)).astype(np.float64)
+    k_rows = rng.integers(-3, 4, (B, S, 128)).astype(np.float64)
+    w = np.ldexp(1.0, rng.integers(-4, 4, B * n_q * H)) * rng.choice([-1.0, 1.0], B * n_q * H)
+    w = w.astype(np.float32)
+    rows = np.arange(B * n_q, dtype=np.int64)
+    got = oracle.logits_exact(q_rows, w, k_rows, ctx, n_q, H, S, rows)
+    for r in range(B * n_q):
+        b, j = divmod(r, n_q)
+        n = max(0, min(int(ctx[b]) - n_q + 1 + j, int(ctx[b])))
+        for s in range(S):
+            if s >= n:
+                assert np.isnan(got[r, s]), (r, s)
+                continue
+            tot = Fraction(0)
+            for h in range(H):
+                d = sum(int(q_rows[r, h, i]) * int(k_rows[b, s, i]) for i in range(128))
+                tot += Fraction(float(w[r * H + h])) * max(d, 0)
+            assert Fraction(got[r, s]) == tot, (r, s)
+
+
+def test_logits_exact_one_hot_and_parallel_closed_forms():
+    """One-hot rows meet only on equal dims; a query head parallel to the key scores
+    c * |k|^2 through the ReLU (zero for c < 0); the weights pick and scale heads."""
+    H = 3
+    k = np.zeros((1, 4, 128), np.float64)
+    for s, i in enumerate((0, 31, 64, 127)):
+        k[0, s, i] = 2.0 ** s
+    q = np.zeros((1, H, 128), np.float64)
+    q[0, 0, 31] = 3.0        # meets token 1 only
+    q[0, 1, 127] = -5.0      # meets token 3 with a negative dot: ReLU gives 0
+    q[0, 2, 64] = 0.5        # meets token 2
+    w = np.array([1.0, 7.0, 4.0], np.float32)
+    got = oracle.logits_exact(q, w, k, np.array([4], np.int32), 1, H, 4, np.array([0], np.int64))[0]
+    np.testing.assert_array_equal(got, [0.0, 1.0 * 3.0 * 2.0, 4.0 * 0.5 * 4.0, 0.0])
+    rng = np.random.default_rng(29)
+    kv = rng.integers(-4, 5, 128).astype(np.float64)
+    norm2 = float(kv @ kv)
+    k2 = kv.reshape(1, 1, 128)
+    coef = np.array([2.0, -1.0, 0.25, 3.0])
+    q2 = (coef[:, None] * kv[None, :]).reshape(1, 4, 128)
+    w2 = np.array([1.0, 100.0, -2.0, 0.5], np.float32)
+    got2 = oracle.logits_exact(q2, w2, k2, np.array([1], np.int32), 1, 4, 1, np.array([0], np.int64))[0, 0]
+    assert got2 == (1.0 * 2.0 + 0.0 - 2.0 * 0.25 + 0.5 * 3.0) * norm2
