@@ -337,14 +337,15 @@ def main():
         bd.idx_logits_paged(pools[i % replicas][1], q, qs, w, pt, ctx, W.B, W.n_q, W.H, W.max_ctx, logits)
 
     def topk(i):
-        bd.idx_topk(logits, ctx, W.B, W.n_q, W.max_ctx, W.topk, out)
+        bd.idx_topk(logits, ctx, W.B, W.n_q, W.topk, out)
 
     def step(i):
         k_store(i)
         score(i)
         topk(i)
 
-    ws = torch.zeros((max(bd.idx_decode_step_workspace_bytes(W.B), 256) // 4,), dtype=torch.int32, device="cuda")
+    ws = torch.zeros((max(bd.idx_workspace_bytes(W.B, W.n_q, W.H, W.max_ctx, W.topk), 256) // 4,), dtype=torch.int32,
+                     device="cuda")
 
     def fused_step(i):
         bd.idx_decode_step(pools[i % replicas][1], k_new, gamma, W.eps, pos_new, cos_sin, slot_new, q, qs, w, pt, ctx,

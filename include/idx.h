@@ -29,6 +29,10 @@
  *  - Device data that breaks the stated contract (a page id outside the pool, a
  *    context length above max_ctx) is never read out of bounds: such pages score
  *    as NaN and lengths are clamped to max_ctx.
+ *  - Scratch memory is the caller's too: the calls that take a (workspace, ws_bytes)
+ *    pair use device memory of at least idx_workspace_bytes(...) bytes, zero-filled
+ *    once before its first use; every call leaves it zero again, so one buffer serves
+ *    every layer and every step (calls sharing it must not overlap in time).
  */
 #ifndef IDX_H
 #define IDX_H
@@ -224,11 +228,15 @@ int idx_q_quant_fp8(const void* q_bf16, const float* w, int64_t n_vecs, uint8_t*
  *                  When n_q * ceil(H/16) > 16 (the prefill form) max_ctx is limited to
  *                  16384 * P (IDX_EUNSUPPORTED beyond).
  * logits           device fp32 [B * n_q][logits_stride].
+ * workspace        device scratch of ws_bytes bytes, sized by idx_workspace_bytes.  No
+ *                  shape this call takes today uses it, so workspace = NULL with
+ *                  ws_bytes = 0 is accepted; a non-NULL workspace must be 256-byte
+ *                  aligned (IDX_EALIGN), and NULL with ws_bytes > 0 is IDX_EINVAL.
  * ------------------------------------------------------------------------------- */
 int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
                      const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
                      int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
-                     void* stream);
+                     void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Per-row top-k of the logits (page "Dense MXFP4 indexer for DeepSeek-V4 on ROCm",
@@ -241,12 +249,30 @@ int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_sc
  *             within the row is unspecified but deterministic (the same input gives the
  *             same bytes).
  * Only cells s < n_r are read.  NaN logits are outside the contract.
- * logits   device fp32 [B * n_q][logits_stride]; ctx_lens device int32 [B];
- * max_ctx  host upper bound of ctx_lens, <= logits_stride; k >= 1;
- * out_idx  device int32 [B * n_q][k].
+ * logits   device fp32 [B * n_q][logits_stride]; logits_stride is also the host bound
+ *          of the row length that sizes the launch (no device read on the host):
+ *          ctx_lens above it are clamped to it; at most 65536 (IDX_EUNSUPPORTED beyond).
+ * ctx_lens device int32 [B];  k >= 1;  out_idx device int32 [B * n_q][k].
+ * workspace, ws_bytes  scratch, with the same rules as for idx_logits_paged (no shape
+ *          this call takes today uses it).
  * ------------------------------------------------------------------------------- */
 int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens, int32_t B, int32_t n_q,
-             int32_t max_ctx, int32_t k, int32_t* out_idx, void* stream);
+             int32_t k, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Device scratch the hot path's calls need for one shape: the largest of what
+ * idx_logits_paged, idx_topk and idx_decode_step take for B sequences of n_q query
+ * rows, H heads, contexts up to max_ctx and top-k k (a multiple of 256; 0 when B, n_q,
+ * H or k is below 1 or max_ctx is negative).  Page "[ROCm][Perf] Add AITER paged MXFP4
+ * sparse indexing on gfx950", Purpose: the cache is read through views with no copies
+ * and the schedule stays fixed under graph replay; page "Dense MXFP4 indexer for
+ * DeepSeek-V4 on ROCm" review discussion: one persistent scratch buffer shared by the
+ * indexer layers.  The buffer is zero-filled once by the caller and every call leaves
+ * it zero (see the conventions above).  Today only idx_decode_step uses it (one block
+ * counter per sequence); the scorer and the top-k keep the pair so that a form needing
+ * scratch changes no caller.
+ * ------------------------------------------------------------------------------- */
+size_t idx_workspace_bytes(int32_t B, int32_t n_q, int32_t H, int32_t max_ctx, int32_t k);
 
 /* ---------------------------------------------------------------------------------
  * Candidate-block scorer: the second level of a two-level indexer, where each query
@@ -306,9 +332,10 @@ int idx_topk_candidates(const float* logits, int64_t logits_stride, const int32_
  *
  * Arguments are those of idx_k_store_* (the pool's format selects MXFP4 or FP8),
  * idx_logits_paged and idx_topk, plus:
- * workspace        device memory of at least idx_decode_step_workspace_bytes(B) bytes,
- *                  4-byte aligned, zero-filled before its first use; every call leaves
- *                  it zero again.  Calls that share a workspace must not overlap.
+ * workspace        device memory of at least idx_workspace_bytes(B, n_q, H, max_ctx, k)
+ *                  bytes, 256-byte aligned, zero-filled before its first use; every call
+ *                  leaves it zero again.  Calls that share a workspace must not overlap
+ *                  (the per-sequence block counters live there).
  * Supported shapes (else IDX_EUNSUPPORTED, before anything is enqueued): the scorer's
  * decode form, n_q * ceil(H/16) <= 16, and max_ctx <= 65536.
  * Execution: one kernel of 1024-thread blocks, each scoring 2048 tokens of a sequence,
@@ -330,8 +357,6 @@ int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride
  * Host-only; for callers and benchmarks that report which kernels ran. */
 int idx_decode_step_fused(int32_t B, int32_t n_q, int32_t H, int32_t max_ctx);
 
-/* Workspace bytes idx_decode_step needs for B sequences (a multiple of 256; 0 if B < 1). */
-size_t idx_decode_step_workspace_bytes(int32_t B);
 
 /* Diagnostic: quot[i] = a[i] / b[i] and root[i] = sqrt(a[i]) in fp64 on the device,
  * with the same division and square-root operations the K store uses, so a test can

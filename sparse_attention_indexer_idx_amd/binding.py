@@ -19,7 +19,7 @@ IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_qk_prep_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
            "idx_logits_paged", "idx_logits_candidates", "idx_topk_candidates",
-           "idx_topk", "idx_decode_step", "idx_decode_step_fused", "idx_decode_step_workspace_bytes", "idx_diag_fp64", "idx_diag_mfma",
+           "idx_topk", "idx_workspace_bytes", "idx_decode_step", "idx_decode_step_fused", "idx_diag_fp64", "idx_diag_mfma",
            "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
 
 
@@ -59,14 +59,14 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_q_prep_mxfp4": [V, I64, I32, V, V, I32, V, F32, V, V, V, V],
         "idx_qk_prep_fp8": [PP, V, V, I64, I32, V, V, V, I32, I32, V, V, F32, V, V, V, V],
         "idx_q_quant_fp8": [V, V, I64, V, V, V],
-        "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V],
-        "idx_topk": [V, I64, V, I32, I32, I32, I32, V, V],
+        "idx_logits_paged": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, V, ctypes.c_size_t, V],
+        "idx_topk": [V, I64, V, I32, I32, I32, V, V, ctypes.c_size_t, V],
+        "idx_workspace_bytes": [I32, I32, I32, I32, I32],
         "idx_logits_candidates": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, V, I32, V, I64, V],
         "idx_topk_candidates": [V, I64, V, I32, I32, I32, I32, I32, V, V],
         "idx_decode_step_fused": [I32, I32, I32, I32],
         "idx_decode_step": [PP, V, I64, V, F32, V, V, I32, V, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, I32,
                             V, V, ctypes.c_size_t, V],
-        "idx_decode_step_workspace_bytes": [I32],
         "idx_diag_fp64": [V, V, V, V, I64, V],
         "idx_diag_mfma": [I32, I32, I32, V, V],
         "idx_device_info": [V, V],
@@ -79,7 +79,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int
     lib.idx_bytes_per_token.restype = ctypes.c_int64
-    lib.idx_decode_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.idx_workspace_bytes.restype = ctypes.c_size_t
     lib.idx_status_string.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
@@ -155,11 +155,20 @@ def idx_q_quant_fp8(q_bf16, w, q_fp8, w_out, stream=None):
                                                      _stream(stream)))
 
 
+def _ws(workspace) -> tuple[int | None, int]:
+    return (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+
+
+def idx_workspace_bytes(B: int, n_q: int, H: int, max_ctx: int, k: int) -> int:
+    return int(load().idx_workspace_bytes(B, n_q, H, max_ctx, k))
+
+
 def idx_logits_paged(pool: IdxPool, q, q_scale, w, page_table, ctx_lens, B: int, n_q: int, H: int, max_ctx: int,
-                     logits, stream=None):
+                     logits, workspace=None, stream=None):
+    ws, wsb = _ws(workspace)
     _check("idx_logits_paged", load().idx_logits_paged(
         ctypes.byref(pool), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1], _ptr(ctx_lens),
-        B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), _stream(stream)))
+        B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), ws, wsb, _stream(stream)))
 
 
 def idx_logits_candidates(pool: IdxPool, q, q_scale, w, page_table, ctx_lens, B: int, n_q: int, H: int, cand_blocks,
@@ -177,9 +186,11 @@ def idx_topk_candidates(logits, cand_blocks, page_size: int, B: int, n_q: int, k
         _stream(stream)))
 
 
-def idx_topk(logits, ctx_lens, B: int, n_q: int, max_ctx: int, k: int, out_idx, stream=None):
-    _check("idx_topk", load().idx_topk(_ptr(logits), logits.stride(0), _ptr(ctx_lens), B, n_q, max_ctx, k,
-                                       _ptr(out_idx), _stream(stream)))
+def idx_topk(logits, ctx_lens, B: int, n_q: int, k: int, out_idx, workspace=None, stream=None):
+    """logits [B*n_q][stride] fp32 (the stride bounds the row length), out_idx [B*n_q][k] int32."""
+    ws, wsb = _ws(workspace)
+    _check("idx_topk", load().idx_topk(_ptr(logits), logits.stride(0), _ptr(ctx_lens), B, n_q, k, _ptr(out_idx), ws,
+                                       wsb, _stream(stream)))
 
 
 def idx_decode_step_fused(B: int, n_q: int, H: int, max_ctx: int) -> int:
@@ -190,21 +201,17 @@ def idx_decode_step_fused(B: int, n_q: int, H: int, max_ctx: int) -> int:
     return r
 
 
-def idx_decode_step_workspace_bytes(B: int) -> int:
-    return int(load().idx_decode_step_workspace_bytes(B))
-
-
 def idx_decode_step(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin, slot_mapping, q, q_scale, w,
                     page_table, ctx_lens, B: int, n_q: int, H: int, max_ctx: int, logits, k: int, out_idx, workspace,
                     stream=None):
     """k_bf16 / positions / slot_mapping hold the B*n_q new rows (row b*n_q + j is token
     ctx[b] - n_q + j of sequence b); workspace is a zero-filled device buffer of at least
-    idx_decode_step_workspace_bytes(B) bytes."""
+    idx_workspace_bytes(B, n_q, H, max_ctx, k) bytes."""
     _check("idx_decode_step", load().idx_decode_step(
         ctypes.byref(pool), _ptr(k_bf16), k_bf16.stride(0), _ptr(gamma), eps, _ptr(positions), _ptr(cos_sin),
         cos_sin.shape[0], _ptr(slot_mapping), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1],
-        _ptr(ctx_lens), B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), k, _ptr(out_idx), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(ctx_lens), B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), k, _ptr(out_idx), *_ws(workspace),
+        _stream(stream)))
 
 
 def idx_diag_fp64(a, b, quot, root, stream=None):

@@ -89,6 +89,17 @@ idx::PoolView view_of(const idx_pool* p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_EHIP; }
 
+// Scratch the fused decode step takes: one block counter per sequence.
+size_t step_workspace_bytes(int32_t B) { return B < 1 ? 0 : ((size_t)B * sizeof(int32_t) + 255) / 256 * 256; }
+
+// A (workspace, ws_bytes) pair for a call that uses `need` bytes of it: NULL only with
+// ws_bytes == 0 and need == 0; a buffer must be 256-byte aligned and large enough.
+int check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return (ws_bytes == 0 && need == 0) ? IDX_OK : IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return IDX_EALIGN;
+  return ws_bytes >= need ? IDX_OK : IDX_EINVAL;
+}
+
 int k_store_common(const idx_pool* pool, int32_t fmt, const void* k_bf16, int64_t n_rows, int64_t row_stride_elems,
                    const float* gamma, float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
                    const int64_t* slot_mapping, void* stream) {
@@ -257,31 +268,33 @@ int logits_args(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, 
 IDX_EXPORT int idx_logits_paged(const idx_pool* pool, const uint8_t* q, const uint8_t* q_scale, const float* w,
                                 const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
                                 int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
-                                int64_t logits_stride, void* stream) {
+                                int64_t logits_stride, void* workspace, size_t ws_bytes, void* stream) {
   idx::LogitsArgs a;
   int st = logits_args(pool, q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, max_ctx, logits,
                        logits_stride, a);
   if (st != IDX_OK) return st;
+  if ((st = check_workspace(workspace, ws_bytes, 0)) != IDX_OK) return st;
   if ((st = check_device()) != IDX_OK) return st;
   return hip_status(idx::launch_logits(a, static_cast<hipStream_t>(stream), num_cus()));
 }
 
 IDX_EXPORT int idx_topk(const float* logits, int64_t logits_stride, const int32_t* ctx_lens, int32_t B, int32_t n_q,
-                        int32_t max_ctx, int32_t k, int32_t* out_idx, void* stream) {
+                        int32_t k, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
   if (!logits || !ctx_lens || !out_idx) return IDX_EINVAL;
-  if (B < 1 || n_q < 1 || k < 1 || max_ctx < 0 || logits_stride < 1) return IDX_EINVAL;
-  if ((int64_t)max_ctx > logits_stride) return IDX_EINVAL;
+  if (B < 1 || n_q < 1 || k < 1 || logits_stride < 1) return IDX_EINVAL;
   if ((int64_t)B * n_q > (int64_t)INT32_MAX) return IDX_EINVAL;
-  if (max_ctx > idx::kTopkMaxCtx) return IDX_EUNSUPPORTED;
-  int st = check_device();
+  // the row capacity bounds the row length and sizes the launch
+  if (logits_stride > idx::kTopkMaxCtx) return IDX_EUNSUPPORTED;
+  int st = check_workspace(workspace, ws_bytes, 0);
   if (st != IDX_OK) return st;
+  if ((st = check_device()) != IDX_OK) return st;
   idx::TopkArgs a;
   a.logits = logits;
   a.lstride = logits_stride;
   a.ctx = ctx_lens;
   a.B = B;
   a.n_q = n_q;
-  a.max_ctx = max_ctx;
+  a.max_ctx = (int32_t)logits_stride;
   a.k = k;
   a.out = out_idx;
   return hip_status(idx::launch_topk(a, static_cast<hipStream_t>(stream)));
@@ -342,28 +355,26 @@ IDX_EXPORT int idx_decode_step_fused(int32_t B, int32_t n_q, int32_t H, int32_t 
   return idx::decode_step_fuses(B, n_q, H, max_ctx, num_cus()) ? 1 : 0;
 }
 
-IDX_EXPORT size_t idx_decode_step_workspace_bytes(int32_t B) {
-  if (B < 1) return 0;
-  return ((size_t)B * sizeof(int32_t) + 255) / 256 * 256;
+IDX_EXPORT size_t idx_workspace_bytes(int32_t B, int32_t n_q, int32_t H, int32_t max_ctx, int32_t k) {
+  if (B < 1 || n_q < 1 || H < 1 || k < 1 || max_ctx < 0) return 0;
+  return step_workspace_bytes(B);
 }
 
-IDX_EXPORT int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
-                               float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
-                               const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
-                               const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
-                               int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
-                               int64_t logits_stride, int32_t k, int32_t* out_idx, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  idx::StepArgs a;
+namespace {
+
+// The decode step's argument checks, all but the scratch's; fills `a` but the counters.
+int decode_step_common(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
+                       float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                       const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                       const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
+                       int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
+                       int32_t k, int32_t* out_idx, idx::StepArgs& a) {
   int st = logits_args(pool, q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, max_ctx, logits,
                        logits_stride, a.s);
   if (st != IDX_OK) return st;
-  if (!k_bf16 || !gamma || !positions || !cos_sin || !slot_mapping || !out_idx || !workspace) return IDX_EINVAL;
+  if (!k_bf16 || !gamma || !positions || !cos_sin || !slot_mapping || !out_idx) return IDX_EINVAL;
   if (row_stride_elems < 128 || !(eps > 0.0f) || max_pos <= 0 || k < 1) return IDX_EINVAL;
-  if (workspace_bytes < idx_decode_step_workspace_bytes(B)) return IDX_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return IDX_EALIGN;
   if (!idx::decode_step_supported(n_q, H, max_ctx)) return IDX_EUNSUPPORTED;
-  if ((st = check_device()) != IDX_OK) return st;
   a.k = static_cast<const uint16_t*>(k_bf16);
   a.row_stride = row_stride_elems;
   a.gamma = gamma;
@@ -374,6 +385,26 @@ IDX_EXPORT int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t
   a.slots = slot_mapping;
   a.k_top = k;
   a.out = out_idx;
+  return IDX_OK;
+}
+
+}  // namespace
+
+IDX_EXPORT int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
+                               float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                               const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                               const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens,
+                               int32_t B, int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits,
+                               int64_t logits_stride, int32_t k, int32_t* out_idx, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  idx::StepArgs a;
+  int st = decode_step_common(pool, k_bf16, row_stride_elems, gamma, eps, positions, cos_sin, max_pos, slot_mapping,
+                              q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, max_ctx, logits,
+                              logits_stride, k, out_idx, a);
+  if (st != IDX_OK) return st;
+  if (!workspace) return IDX_EINVAL;
+  if ((st = check_workspace(workspace, workspace_bytes, step_workspace_bytes(B))) != IDX_OK) return st;
+  if ((st = check_device()) != IDX_OK) return st;
   a.counters = static_cast<int32_t*>(workspace);
   return hip_status(idx::launch_decode_step(a, static_cast<hipStream_t>(stream), num_cus()));
 }

@@ -66,7 +66,8 @@ def logits_call(lib, p=None, **kw):
     a.update(kw)
     p = p or pool()
     return lib.idx_logits_paged(ctypes.byref(p), a["q"], a["qs"], a["w"], a["pt"], a["maxp"], a["ctx"], a["B"],
-                                a["n_q"], a["H"], a["D"], a["max_ctx"], a["logits"], a["lstride"], None)
+                                a["n_q"], a["H"], a["D"], a["max_ctx"], a["logits"], a["lstride"], a.get("ws"),
+                                ctypes.c_size_t(a.get("wsb", 0)), None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -81,6 +82,8 @@ def logits_call(lib, p=None, **kw):
     (dict(lstride=100), bd.IDX_EINVAL),      # < max_ctx
     (dict(max_ctx=-1), bd.IDX_EINVAL),
     (dict(q=FAKE + 8), bd.IDX_EALIGN),
+    (dict(ws=None, wsb=256), bd.IDX_EINVAL),         # a size with no buffer
+    (dict(ws=FAKE + 64, wsb=256), bd.IDX_EALIGN),    # scratch must be 256-byte aligned
 ])
 def test_logits_argument_checks(lib, kw, want):
     assert logits_call(lib, **kw) == want
@@ -121,12 +124,30 @@ def test_k_store_checks(lib):
     assert call(lib.idx_k_store_mxfp4, p=pool(kv_format=1, page_stride_bytes=132 * 64)) == bd.IDX_EINVAL
 
 
+def topk_call(lib, **kw):
+    a = dict(lg=FAKE, ls=256, ctx=FAKE, B=2, n_q=1, k=64, out=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return lib.idx_topk(a["lg"], a["ls"], a["ctx"], a["B"], a["n_q"], a["k"], a["out"], a["ws"],
+                        ctypes.c_size_t(a["wsb"]), None)
+
+
 def test_topk_checks(lib):
-    f = lib.idx_topk
-    assert f(None, 256, FAKE, 2, 1, 256, 64, FAKE, None) == bd.IDX_EINVAL
-    assert f(FAKE, 256, FAKE, 2, 1, 257, 64, FAKE, None) == bd.IDX_EINVAL
-    assert f(FAKE, 256, FAKE, 2, 1, 256, 0, FAKE, None) == bd.IDX_EINVAL
-    assert f(FAKE, 1 << 20, FAKE, 2, 1, 65537, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
+    assert topk_call(lib, lg=None) == bd.IDX_EINVAL
+    assert topk_call(lib, ls=0) == bd.IDX_EINVAL
+    assert topk_call(lib, k=0) == bd.IDX_EINVAL
+    assert topk_call(lib, B=0) == bd.IDX_EINVAL
+    assert topk_call(lib, ls=65537) == bd.IDX_EUNSUPPORTED      # rows beyond the register-held limit
+    assert topk_call(lib, ws=None, wsb=512) == bd.IDX_EINVAL
+    assert topk_call(lib, ws=FAKE + 16, wsb=512) == bd.IDX_EALIGN
+
+
+def test_workspace_bytes(lib):
+    f = lib.idx_workspace_bytes
+    assert f(0, 1, 32, 8192, 1024) == 0 and f(1, 0, 32, 8192, 1024) == 0 and f(1, 1, 0, 8192, 1024) == 0
+    assert f(1, 1, 32, -1, 1024) == 0 and f(1, 1, 32, 8192, 0) == 0
+    # one block counter per sequence, in 256-byte units
+    assert f(1, 1, 32, 8192, 1024) == 256 and f(64, 1, 32, 8192, 1024) == 256 and f(65, 1, 32, 8192, 1024) == 512
+    assert all(f(B, 3, 64, 2368, 1024) % 256 == 0 for B in (1, 63, 64, 128, 1000))
 
 
 def step_call(lib, p=None, **kw):
@@ -134,7 +155,7 @@ def step_call(lib, p=None, **kw):
     P = p if p is not None else pool()
     d = dict(k=FAKE, rs=128, g=FAKE, eps=1e-6, pos=FAKE, cs=FAKE, mp=512, sl=FAKE, q=FAKE, qs=FAKE, w=FAKE, pt=FAKE,
              mpp=4, ctx=FAKE, B=2, n_q=1, H=32, D=128, mc=256, lg=FAKE, ls=256, kk=64, out=FAKE, ws=FAKE,
-             wsb=lib.idx_decode_step_workspace_bytes(2))
+             wsb=lib.idx_workspace_bytes(2, 1, 32, 256, 64))
     d.update(kw)
     return lib.idx_decode_step(ctypes.byref(P), d["k"], d["rs"], d["g"], ctypes.c_float(d["eps"]), d["pos"], d["cs"],
                                d["mp"], d["sl"], d["q"], d["qs"], d["w"], d["pt"], d["mpp"], d["ctx"], d["B"],
@@ -152,11 +173,11 @@ def test_decode_step_fused_query(lib):
 
 
 def test_decode_step_checks(lib):
-    assert lib.idx_decode_step_workspace_bytes(0) == 0
-    assert lib.idx_decode_step_workspace_bytes(1) == 256 and lib.idx_decode_step_workspace_bytes(65) == 512
     assert step_call(lib, ws=None) == bd.IDX_EINVAL
     assert step_call(lib, wsb=0) == bd.IDX_EINVAL
+    assert step_call(lib, wsb=255) == bd.IDX_EINVAL
     assert step_call(lib, ws=FAKE + 2) == bd.IDX_EALIGN
+    assert step_call(lib, ws=FAKE + 128) == bd.IDX_EALIGN
     assert step_call(lib, sl=None) == bd.IDX_EINVAL
     assert step_call(lib, rs=64) == bd.IDX_EINVAL
     assert step_call(lib, kk=0) == bd.IDX_EINVAL
@@ -201,7 +222,7 @@ def test_valid_calls_report_missing_device(lib):
     if not no_gpu(lib):
         pytest.skip("a GPU is present: fake pointers must not reach a launch")
     assert logits_call(lib) == bd.IDX_EUNSUPPORTED
-    assert lib.idx_topk(FAKE, 256, FAKE, 2, 1, 256, 64, FAKE, None) == bd.IDX_EUNSUPPORTED
+    assert topk_call(lib) == bd.IDX_EUNSUPPORTED
     assert lib.idx_q_quant_mxfp4(FAKE, 4, FAKE, FAKE, None) == bd.IDX_EUNSUPPORTED
     # zero-sized work still goes through the device gate
     assert lib.idx_device_check() == bd.IDX_EUNSUPPORTED

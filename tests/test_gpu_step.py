@@ -53,7 +53,8 @@ class Step:
         self.slot_np = np.where(have, W.slots[src], -1).astype(np.int64)
         self.slot_d = G.dev(self.slot_np)
         self.gamma_d, self.cs_d = G.dev(W.gamma), G.dev(W.cos_sin)
-        self.ws = torch.zeros(bd.idx_decode_step_workspace_bytes(W.B) // 4, dtype=torch.int32, device="cuda")
+        self.ws = torch.zeros(bd.idx_workspace_bytes(W.B, W.n_q, W.H, W.max_ctx, W.topk) // 4, dtype=torch.int32,
+                              device="cuda")
 
     def buffers(self):
         torch = G.torch_cuda()
@@ -79,7 +80,7 @@ class Step:
         store(self.pool.view, self.k_d, self.gamma_d, W.eps, self.pos_d, self.cs_d, self.slot_d)
         bd.idx_logits_paged(self.pool.view, self.q_d, self.qs_d, self.w_d, self.pt_d, self.ctx_d, W.B, W.n_q, W.H,
                             W.max_ctx, logits)
-        bd.idx_topk(logits, self.ctx_d, W.B, W.n_q, W.max_ctx, W.topk, out)
+        bd.idx_topk(logits, self.ctx_d, W.B, W.n_q, W.topk, out)
         G.torch_cuda().cuda.synchronize()
         return logits.cpu().numpy(), out.cpu().numpy()
 
