@@ -49,7 +49,8 @@ typedef enum {
   IDX_EINVAL = -1,
   IDX_EUNSUPPORTED = -2,
   IDX_EALIGN = -3,
-  IDX_EHIP = -4
+  IDX_EHIP = -4,
+  IDX_ESCRATCH = -5 /* the call needs more scratch than the library's static array holds */
 } idx_status;
 
 /* Indexer K-cache formats.
@@ -350,6 +351,26 @@ int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t row_stride
                     const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
                     int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
                     int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * The fused decode step for callers that cannot allocate device memory (code under HIP
+ * graph capture that must not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation): idx_decode_step with the same arguments and results, minus the workspace.
+ * Its per-sequence block counters live in a static device array inside this library
+ * (IDX_NOALLOC_MAX_SEQS int32 counters, 64 KiB per device, held by every device the
+ * library runs on until the process ends); the caller still passes every input and
+ * output.  The array starts zero and every call leaves it zero.  Calls that overlap in
+ * time on one device share the array and race: serialise them (one stream, or events).
+ * IDX_ESCRATCH when B > IDX_NOALLOC_MAX_SEQS; IDX_EHIP if the array's device address
+ * cannot be obtained; otherwise the statuses of idx_decode_step.  Allocates nothing.
+ * ------------------------------------------------------------------------------- */
+#define IDX_NOALLOC_MAX_SEQS 16384
+int idx_decode_step_noalloc(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
+                            float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                            const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
+                            const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B,
+                            int32_t n_q, int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
+                            int32_t k, int32_t* out_idx, void* stream);
 
 /* How idx_decode_step runs this shape on the current device: 1 = the one fused kernel,
  * 0 = the K store, scorer and top-k kernels in sequence; IDX_EUNSUPPORTED for a shape it

@@ -14,12 +14,13 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libidx.so")
 
-IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP = 0, -1, -2, -3, -4
+IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_EHIP, IDX_ESCRATCH = 0, -1, -2, -3, -4, -5
+IDX_NOALLOC_MAX_SEQS = 16384
 IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_qk_prep_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
            "idx_logits_paged", "idx_logits_candidates", "idx_topk_candidates",
-           "idx_topk", "idx_workspace_bytes", "idx_decode_step", "idx_decode_step_fused", "idx_diag_fp64", "idx_diag_mfma",
+           "idx_topk", "idx_workspace_bytes", "idx_decode_step", "idx_decode_step_noalloc", "idx_decode_step_fused", "idx_diag_fp64", "idx_diag_mfma",
            "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
 
 
@@ -65,6 +66,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "idx_logits_candidates": [PP, V, V, V, V, I32, V, I32, I32, I32, I32, V, I32, V, I64, V],
         "idx_topk_candidates": [V, I64, V, I32, I32, I32, I32, I32, V, V],
         "idx_decode_step_fused": [I32, I32, I32, I32],
+        "idx_decode_step_noalloc": [PP, V, I64, V, F32, V, V, I32, V, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V,
+                                    I64, I32, V, V],
         "idx_decode_step": [PP, V, I64, V, F32, V, V, I32, V, V, V, V, V, I32, V, I32, I32, I32, I32, I32, V, I64, I32,
                             V, V, ctypes.c_size_t, V],
         "idx_diag_fp64": [V, V, V, V, I64, V],
@@ -212,6 +215,17 @@ def idx_decode_step(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin
         cos_sin.shape[0], _ptr(slot_mapping), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1],
         _ptr(ctx_lens), B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), k, _ptr(out_idx), *_ws(workspace),
         _stream(stream)))
+
+
+def idx_decode_step_noalloc(pool: IdxPool, k_bf16, gamma, eps: float, positions, cos_sin, slot_mapping, q, q_scale,
+                            w, page_table, ctx_lens, B: int, n_q: int, H: int, max_ctx: int, logits, k: int, out_idx,
+                            stream=None):
+    """idx_decode_step without a workspace: the block counters live in the library's own
+    static device array (B <= IDX_NOALLOC_MAX_SEQS)."""
+    _check("idx_decode_step_noalloc", load().idx_decode_step_noalloc(
+        ctypes.byref(pool), _ptr(k_bf16), k_bf16.stride(0), _ptr(gamma), eps, _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(slot_mapping), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(page_table), page_table.shape[1],
+        _ptr(ctx_lens), B, n_q, H, 128, max_ctx, _ptr(logits), logits.stride(0), k, _ptr(out_idx), _stream(stream)))
 
 
 def idx_diag_fp64(a, b, quot, root, stream=None):

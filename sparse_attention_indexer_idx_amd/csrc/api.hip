@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "idx.h"
 #include "launch.hpp"
@@ -362,7 +363,8 @@ IDX_EXPORT size_t idx_workspace_bytes(int32_t B, int32_t n_q, int32_t H, int32_t
 
 namespace {
 
-// The decode step's argument checks, all but the scratch's; fills `a` but the counters.
+// Everything idx_decode_step and idx_decode_step_noalloc share: the argument checks, all
+// but the scratch's; fills `a` but the counters.
 int decode_step_common(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems, const float* gamma,
                        float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos,
                        const int64_t* slot_mapping, const uint8_t* q, const uint8_t* q_scale, const float* w,
@@ -406,6 +408,66 @@ IDX_EXPORT int idx_decode_step(const idx_pool* pool, const void* k_bf16, int64_t
   if ((st = check_workspace(workspace, workspace_bytes, step_workspace_bytes(B))) != IDX_OK) return st;
   if ((st = check_device()) != IDX_OK) return st;
   a.counters = static_cast<int32_t*>(workspace);
+  return hip_status(idx::launch_decode_step(a, static_cast<hipStream_t>(stream), num_cus()));
+}
+
+// ---------------------------------------------------------------------------------------
+// The decode step for callers that cannot allocate: its block counters live in this
+// library's own device array.  The array has static storage (zero when the code object
+// loads), every device holds its own copy at its own address, and its device address is
+// taken once per device with hipGetSymbolAddress on the entry point's first call there.
+// Every call leaves the counters it used at zero (the last block of each sequence resets
+// its counter), so each call finds them cleared.  Calls that overlap on one device share
+// the array and race.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) int32_t scratch[IDX_NOALLOC_MAX_SEQS];
+
+std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (nullptr if it cannot be had).
+int32_t* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  p = static_cast<int32_t*>(addr);
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+IDX_EXPORT int idx_decode_step_noalloc(const idx_pool* pool, const void* k_bf16, int64_t row_stride_elems,
+                                       const float* gamma, float eps, const int32_t* positions, const float* cos_sin,
+                                       int32_t max_pos, const int64_t* slot_mapping, const uint8_t* q,
+                                       const uint8_t* q_scale, const float* w, const int32_t* page_table,
+                                       int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t B, int32_t n_q,
+                                       int32_t H, int32_t D, int32_t max_ctx, float* logits, int64_t logits_stride,
+                                       int32_t k, int32_t* out_idx, void* stream) {
+  idx::StepArgs a;
+  int st = decode_step_common(pool, k_bf16, row_stride_elems, gamma, eps, positions, cos_sin, max_pos, slot_mapping,
+                              q, q_scale, w, page_table, max_pages_per_seq, ctx_lens, B, n_q, H, D, max_ctx, logits,
+                              logits_stride, k, out_idx, a);
+  if (st != IDX_OK) return st;
+  if (B > IDX_NOALLOC_MAX_SEQS) return IDX_ESCRATCH;
+  if ((st = check_device()) != IDX_OK) return st;
+  int32_t* counters = scratch_for_current_device();
+  if (!counters) return IDX_EHIP;
+  a.counters = counters;
   return hip_status(idx::launch_decode_step(a, static_cast<hipStream_t>(stream), num_cus()));
 }
 
@@ -453,6 +515,7 @@ IDX_EXPORT const char* idx_status_string(int status) {
     case IDX_EUNSUPPORTED: return "unsupported shape, page size or device (needs gfx950, head dim 128)";
     case IDX_EALIGN: return "misaligned pool offset, page stride or buffer";
     case IDX_EHIP: return "HIP runtime error while enqueueing";
+    case IDX_ESCRATCH: return "more sequences than the library's static scratch holds (idx_decode_step_noalloc)";
     default: return "unknown status";
   }
 }
