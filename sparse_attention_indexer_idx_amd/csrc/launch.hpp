@@ -100,9 +100,12 @@ hipError_t launch_q_quant_mxfp4(const uint16_t* q, int64_t n_vecs, uint8_t* qp, 
 hipError_t launch_q_quant_fp8(const uint16_t* q, const float* w, int64_t n_vecs, uint8_t* q8, float* wo,
                               hipStream_t s);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t s, int num_cus = 256);
-// Streaming decode scorer: one query row per wave over a strided set of 64-token chunks,
-// the next chunk's K in flight while the current one is scored (n_q <= 4).
+// Streaming decode scorer: workers (a wave for n_q = 1, a block of n_q row waves for
+// n_q = 2..4) take balanced contiguous runs of 64-token chunks of one sequence, the next
+// chunk's K in flight while the current one is scored.
 hipError_t launch_logits_stream(const LogitsArgs& a, int num_cus, hipStream_t s);
+// Whether the streaming scorer takes this shape (n_q <= 4, B <= 1024, chunk counts in int32).
+bool logits_stream_takes(int B, int n_q, int max_ctx);
 // Whether the scorer takes its decode form (all query rows of a sequence in registers).
 bool logits_uses_decode_kernel(int n_q, int H);
 // Largest max_ctx the scorer accepts for this shape (the prefill form splits the context
@@ -158,6 +161,8 @@ hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus);
 // 8 * rounds MFMAs (16x16x128, fmt 0: E2M1 x E2M1, 1: e4m3 x e4m3) per wave on register
 // operands; out gets blocks * 256 floats.
 hipError_t launch_diag_mfma(int fmt, int blocks, int rounds, float* out, hipStream_t s);
+// Plain streaming read of `bytes` (a multiple of 16) at buf; out gets blocks * 256 floats.
+hipError_t launch_diag_read(const void* buf, int64_t bytes, int blocks, float* out, hipStream_t s);
 hipError_t launch_diag_fp64(const double* a, const double* b, double* quot, double* root, int64_t n,
                             hipStream_t s);
 

@@ -316,13 +316,11 @@ hipError_t launch_logits(const LogitsArgs& args, hipStream_t s, int num_cus) {
   if (args.max_ctx == 0) return hipSuccess;
   const LogitsArgs& a = args;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
-  // several query rows with many heads: the streaming row-split form (its chunk indices
-  // stay well inside int32 for contexts up to 2^30 tokens)
-  const bool stream_ok = a.max_ctx <= (1 << 30);
-  if (stream_ok && a.n_q > 1 && a.n_q <= 4 && a.n_q * ht > 4) return launch_logits_stream(a, num_cus, s);
+  // several query rows with many heads: the streaming form with balanced runs
+  const bool stream_ok = logits_stream_takes(a.B, a.n_q, a.max_ctx);
+  if (stream_ok && a.n_q > 1 && a.n_q * ht > 4) return launch_logits_stream(a, num_cus, s);
   // one row per sequence over many tokens (mixed lengths likely): the streaming form too,
-  // with non-temporal K loads (measured: B256 with 4K-16K contexts 46.3 -> 41.7 us; on
-  // B64/8K the one-pass kernel stays faster, 8.5 vs 9.5 us)
+  // with non-temporal K loads (on B64/8K the one-pass kernel stays faster)
   if (stream_ok && a.n_q == 1 && (int64_t)a.B * a.max_ctx >= kStreamTokens) return launch_logits_stream(a, num_cus, s);
   if (logits_uses_decode_kernel(a.n_q, a.H))
     return a.pool.kv_format == 0 ? launch_decode<0>(a, a.n_q * ht, s) : launch_decode<1>(a, a.n_q * ht, s);

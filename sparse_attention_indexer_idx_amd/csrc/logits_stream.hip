@@ -1,16 +1,19 @@
-// Streaming form of the decode scorer (gfx950): each wave scores one query row over a
-// strided set of 64-token chunks of its sequence, with the next chunk's K tiles in
-// flight while the current one is scored (two register buffers used alternately, so no
-// register copy waits on a load).  For shapes where one pass of short-lived waves leaves
-// the memory system idle while they compute: several query rows with many heads (e.g. 3
-// speculative tokens x 64 heads) over mixed context lengths.
+// Streaming form of the decode scorer (gfx950) for shapes where one pass of short-lived
+// waves leaves the memory system idle while they compute: several query rows with many
+// heads (e.g. 3 speculative tokens x 64 heads) and long, mixed context lengths.
 //
-// Blocks of 4 waves; wave w takes row w % n_q and chunk lane w / n_q of its block (n_q <= 4;
-// waves past n_q * floor(4 / n_q) leave at once), so the rows of a chunk run on one CU and
-// all but one read its K from the cache.  Chunk c of row j covers tokens [64c, 64c + 64);
-// block x's chunk lane l takes chunks x*L + l, x*L + l + S, ... (L lanes per block, S =
-// gridDim.x * L) below the row's valid length.  Loads are issued for every step, past the
-// end too (page 0 row 0), so the outstanding-load count is the same on every path.
+// Work is balanced across workers from the device-side lengths, with no host read: a
+// sequence of n_b tokens has ceil(n_b / 64) chunks of 64 tokens; with U chunks in all and
+// W workers, every worker takes a contiguous run of at most q = ceil(U / (W - B)) chunks of
+// one sequence (sequence b gets ceil(chunks_b / q) workers), so long and short sequences
+// finish together and a worker's query tiles stay the same throughout its run.  Each wave
+// computes U, q and its own run from the lengths (a wave-wide prefix over the sequences).
+// A worker is a wave when n_q = 1; for n_q = 2..4 it is a block whose wave j scores query
+// row j of the same chunks, so the rows of a chunk run on one CU and all but one read its
+// K from the cache.  Within a run, the next chunk's K tiles are in flight while the
+// current one is scored (two register buffers used alternately); loads are issued on every
+// step, past the run too (page 0 row 0), so the outstanding-load count is the same on every
+// path.
 #include <algorithm>
 
 #include "scorer.hpp"
@@ -18,16 +21,72 @@
 namespace idx {
 namespace {
 
-template <int FMT, int HT, bool NT_LOADS>
+constexpr int kStreamMaxSeqs = 64 * 16;  // sequences a wave's prefix covers (16 per lane)
+
+// The worker's run: sequence b and chunks [c0, c1) (c0 >= c1: no work).  Every lane of
+// the wave gets the same values.  Lane l holds sequences [l*m, l*m + m).
+template <int M>
+__device__ __forceinline__ void worker_run(const LogitsArgs& a, int worker, int n_workers, int lane, int& b, int& c0,
+                                           int& c1) {
+  int ch[M];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int s = lane * M + i;
+    const int n = s < a.B ? std::min(std::max(a.ctx[s], 0), a.max_ctx) : 0;
+    ch[i] = (n + 63) >> 6;
+    sum += ch[i];
+  }
+  const int total = __builtin_amdgcn_readlane(wave_incl_scan(sum), 63);  // U (< 2^31: checked on the host)
+  const int spare = std::max(n_workers - a.B, 1);
+  const int q = std::max(1, (total + spare - 1) / spare);  // chunks per worker
+  int wsum = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) wsum += (ch[i] + q - 1) / q;
+  const int wincl = wave_incl_scan(wsum);
+  const int wexcl = wincl - wsum;
+  const uint64_t hit = __ballot(wexcl <= worker && worker < wincl);
+  b = -1;
+  c0 = c1 = 0;
+  if (hit == 0) return;  // past the last run (uniform)
+  const int L = __builtin_ctzll(hit);
+  int bb = 0, cc0 = 0, cc1 = 0;
+  if (lane == L) {
+    int before = wexcl;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int wi = (ch[i] + q - 1) / q;
+      if (before <= worker && worker < before + wi) {
+        bb = lane * M + i;
+        cc0 = (worker - before) * q;
+        cc1 = std::min(cc0 + q, ch[i]);
+      }
+      before += wi;
+    }
+  }
+  b = __builtin_amdgcn_readlane(bb, L);
+  c0 = __builtin_amdgcn_readlane(cc0, L);
+  c1 = __builtin_amdgcn_readlane(cc1, L);
+}
+
+template <int FMT, int HT, bool NT_LOADS, int M>
 __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int lanes_per_block = 4 / a.n_q;
-  if (wave >= a.n_q * lanes_per_block) return;
-  const int j = wave % a.n_q, cl = wave / a.n_q;
-  const int b = blockIdx.y;
-  const int stride = (int)gridDim.x * lanes_per_block;
-  int c = (int)blockIdx.x * lanes_per_block + cl;
+  int worker, n_workers, j;
+  if (a.n_q == 1) {
+    worker = blockIdx.x * 4 + wave;
+    n_workers = gridDim.x * 4;
+    j = 0;
+  } else {
+    if (wave >= a.n_q) return;
+    worker = blockIdx.x;
+    n_workers = gridDim.x;
+    j = wave;
+  }
+  int b, c, c_end;
+  worker_run<M>(a, worker, n_workers, lane, b, c, c_end);
+  if (b < 0 || c >= c_end) return;  // uniform: no run for this worker
   const int64_t r = (int64_t)b * a.n_q + j;
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int last_page = (a.max_ctx - 1) >> lgP;
@@ -43,8 +102,7 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   }
   const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
   const int n_r = valid_len(n_b, a.n_q, j);
-  const int n_ch = (n_r + 63) >> 6;
-  if (c >= n_ch) return;  // uniform: nothing to score
+  const int n_ch = std::min((n_r + 63) >> 6, c_end);  // this row's chunks inside the run
 
   const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);  // page ids are int32
   // Issue the four K tiles of chunk cc (any cc: past the row they read page 0 row 0).
@@ -90,15 +148,16 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
     if (s < n_r) out_row[s] = logit;
   };
 
+  if (c >= n_ch) return;  // uniform: this row ends before the run (rows j < n_q - 1)
   KTile<FMT> A[4], B[4];
   bool okA[4], okB[4];
   issue(c, A, okA);
   for (;;) {
-    const int c2 = c + stride;
+    const int c2 = c + 1;
     issue(c2, B, okB);
     consume(c, A, okA);
     if (c2 >= n_ch) break;  // uniform
-    const int c3 = c2 + stride;
+    const int c3 = c2 + 1;
     issue(c3, A, okA);
     consume(c2, B, okB);
     if (c3 >= n_ch) break;
@@ -106,13 +165,13 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   }
 }
 
-template <int FMT>
-hipError_t launch_stream_fmt(const LogitsArgs& a, dim3 grid, int ht, hipStream_t s) {
+template <int FMT, int M>
+hipError_t launch_stream_m(const LogitsArgs& a, dim3 grid, int ht, hipStream_t s) {
   switch (ht) {
 #define IDX_STREAM_CASE(N) \
   case N: \
-    if (a.n_q == 1) hipLaunchKernelGGL((logits_stream_kernel<FMT, N, true>), grid, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((logits_stream_kernel<FMT, N, false>), grid, dim3(256), 0, s, a); \
+    if (a.n_q == 1) hipLaunchKernelGGL((logits_stream_kernel<FMT, N, true, M>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((logits_stream_kernel<FMT, N, false, M>), grid, dim3(256), 0, s, a); \
     break;
     IDX_STREAM_CASE(1) IDX_STREAM_CASE(2) IDX_STREAM_CASE(3) IDX_STREAM_CASE(4)
     IDX_STREAM_CASE(5) IDX_STREAM_CASE(6) IDX_STREAM_CASE(7) IDX_STREAM_CASE(8)
@@ -122,22 +181,38 @@ hipError_t launch_stream_fmt(const LogitsArgs& a, dim3 grid, int ht, hipStream_t
   return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t launch_stream_fmt(const LogitsArgs& a, dim3 grid, int ht, hipStream_t s) {
+  const int m = (a.B + 63) / 64;
+  if (m <= 1) return launch_stream_m<FMT, 1>(a, grid, ht, s);
+  if (m <= 2) return launch_stream_m<FMT, 2>(a, grid, ht, s);
+  if (m <= 4) return launch_stream_m<FMT, 4>(a, grid, ht, s);
+  if (m <= 8) return launch_stream_m<FMT, 8>(a, grid, ht, s);
+  return launch_stream_m<FMT, 16>(a, grid, ht, s);
+}
+
 }  // namespace
+
+bool logits_stream_takes(int B, int n_q, int max_ctx) {
+  // the wave-wide prefix covers up to 1024 sequences; chunk counts stay inside int32
+  return n_q >= 1 && n_q <= 4 && B >= 1 && B <= kStreamMaxSeqs && max_ctx <= (1 << 30) &&
+         (int64_t)B * ((max_ctx + 63) / 64) < ((int64_t)1 << 31);
+}
 
 hipError_t launch_logits_stream(const LogitsArgs& a, int num_cus, hipStream_t s) {
   if (a.max_ctx == 0) return hipSuccess;
-  if (a.n_q < 1 || a.n_q > 4) return hipErrorInvalidValue;
+  if (!logits_stream_takes(a.B, a.n_q, a.max_ctx)) return hipErrorInvalidValue;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
-  const int lanes = 4 / a.n_q;
-  const int chunks = (a.max_ctx + 63) / 64;
-  // about eight waves per SIMD over the device, and at least four chunks per wave (measured
-  // on 3 tokens x 64 heads: 13.3, 12.5 and 15.5 us for two, four and eight)
+  // About eight waves per SIMD over the device, at least two workers per sequence (so the
+  // balanced runs have room), and no more workers than chunks.
+  const int64_t max_units = (int64_t)a.B * ((a.max_ctx + 63) / 64);
   const int64_t want_waves = (int64_t)num_cus * 32;
-  const int64_t row_waves = (int64_t)a.B * a.n_q;
-  int64_t bx = std::max<int64_t>(1, want_waves / std::max<int64_t>(1, row_waves * lanes));
-  bx = std::min<int64_t>(bx, std::max(1, (chunks + 4 * lanes - 1) / (4 * lanes)));
-  const dim3 grid((unsigned)bx, (unsigned)a.B);
-  return a.pool.kv_format == 0 ? launch_stream_fmt<0>(a, grid, ht, s) : launch_stream_fmt<1>(a, grid, ht, s);
+  int64_t workers = a.n_q == 1 ? want_waves : want_waves / 4;
+  workers = std::max<int64_t>(workers, 2 * (int64_t)a.B);
+  workers = std::min<int64_t>(workers, max_units + a.B);
+  const int64_t blocks = a.n_q == 1 ? (workers + 3) / 4 : workers;
+  return a.pool.kv_format == 0 ? launch_stream_fmt<0>(a, dim3((unsigned)blocks), ht, s)
+                               : launch_stream_fmt<1>(a, dim3((unsigned)blocks), ht, s);
 }
 
 }  // namespace idx

@@ -24,14 +24,26 @@
 namespace idx {
 
 
-// Order-preserving key of a valid cell, never 0: -0.0 ranks equal to +0.0, and the one
-// pattern that would map to 0 (a negative NaN) shares key 1 with its neighbour.  Key 0
-// marks a cell past the row's valid length, so that cell ranks below every valid one.
-__device__ __forceinline__ uint32_t float_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return k == 0u ? 1u : k;
+// Order-preserving 32-bit key of an fp32 logit, by arithmetic only (no compare, so no
+// lane mask stays live across a row's unrolled rounds): adding +0.0 turns -0.0 into
+// +0.0 (denormals are kept: the kernels run with fp32 denormals on), then non-negative
+// values get the sign bit set and negative ones are complemented.  Key 0 is reserved
+// for a cell that is not a candidate (past the row's valid length), which then ranks
+// below every valid one; the one fp32 pattern that would map to 0 (a negative NaN with
+// every payload bit set) takes key 1 in dense rows.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// All ones when rel < 0 (a cell index below the row's length), else 0.  The empty asm
+// keeps the mask an opaque register value: as a plain shift the compiler rewrites the
+// masking as a compare and select, and then keeps one 64-bit lane mask per unrolled round
+// live in scalar registers, which spill.
+__device__ __forceinline__ uint32_t below_mask(int rel) {
+  uint32_t m = (uint32_t)(rel >> 31);
+  asm volatile("" : "+v"(m));
+  return m;
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
@@ -109,37 +121,71 @@ __device__ __forceinline__ void block_excl_scan2(int v0, int v1, int32_t* wave_t
 
 // Given a histogram of BINS digits (BINS >= NT), find the digit d holding the kk-th
 // largest item (kk >= 1): count(digits > d) < kk <= count(digits >= d).  Thread t covers
-// BINS/NT digits, the highest to thread 0; only the thread whose range holds the answer
-// re-reads its bins.  Leaves d and count(> d) in shared memory (two barriers).
+// BINS/NT consecutive digits, the highest to thread 0, read as 16-byte words and kept in
+// registers; only the thread whose range holds the answer walks its bins.  Leaves d and
+// count(> d) in shared memory (two barriers).
 template <int NT, int BINS, class SH>
 __device__ __forceinline__ void select_digit(SH& sh, int kk) {
   constexpr int PER = BINS / NT;
-  const int hi = BINS - PER * (int)threadIdx.x;  // digits [hi - PER, hi)
+  const int lo = BINS - PER * ((int)threadIdx.x + 1);  // digits [lo, lo + PER)
+  uint32_t c[PER];
+  if constexpr (PER % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(sh.hist + lo)[q];
+      c[4 * q] = v.x;
+      c[4 * q + 1] = v.y;
+      c[4 * q + 2] = v.z;
+      c[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) c[q] = sh.hist[lo + q];
+  }
   int local = 0;
 #pragma unroll
-  for (int q = 0; q < PER; ++q) local += (int)sh.hist[hi - 1 - q];
+  for (int q = 0; q < PER; ++q) local += (int)c[q];
   int total;
   int before = block_excl_scan<NT>(local, sh.wave_tot, total);
   if (before < kk && kk <= before + local) {
-    for (int q = 0; q < PER; ++q) {
-      const int c = (int)sh.hist[hi - 1 - q];
-      if (before < kk && kk <= before + c) {
-        sh.sel_digit = hi - 1 - q;
+#pragma unroll
+    for (int q = PER - 1; q >= 0; --q) {
+      const int cq = (int)c[q];
+      if (before < kk && kk <= before + cq) {
+        sh.sel_digit = lo + q;
         sh.sel_above = before;
       }
-      before += c;
+      before += cq;
     }
   }
   __syncthreads();
+}
+
+// Runs f(e) for every round e < EPT whose group of 8 rounds holds a valid cell: a group
+// wholly past ne (the rounds holding valid cells) is skipped by one uniform branch, and
+// inside a group every round runs (a round past ne holds only key 0, which no phase
+// selects), so no per-round condition has to stay live across the unrolled loops.
+template <int EPT, class F>
+__device__ __forceinline__ void for_rounds(int ne, F&& f) {
+#pragma unroll
+  for (int g = 0; g < EPT; g += 8) {
+    if (g == 0 || g < ne) {
+#pragma unroll
+      for (int e = g; e < (g + 8 < EPT ? g + 8 : EPT); ++e) f(e);
+    }
+  }
 }
 
 // How a row's cells become keys and output indices.  DenseRow: every cell below n is
 // valid and is its own token index.  CandidateRow: cell c*P + i is token
 // cand[c]*P + i, and a cell holding -inf is not a candidate (the candidate scorer writes
 // -inf there), so the number of valid cells is only known once the keys are formed.
+// key(f, rel): the key of cell value f, where rel = cell - n (negative inside the row).
 struct DenseRow {
   static constexpr bool kCountValid = false;
-  __device__ __forceinline__ uint32_t key(float f) const { return float_key(f); }
+  __device__ __forceinline__ uint32_t key(float f, int rel) const {
+    return max(order_key(f), 1u) & below_mask(rel);
+  }
   __device__ __forceinline__ int32_t token(int cell) const { return cell; }
 };
 
@@ -147,122 +193,45 @@ struct CandidateRow {
   static constexpr bool kCountValid = true;
   const int32_t* cand;
   int32_t page_shift;
-  __device__ __forceinline__ uint32_t key(float f) const { return f == -__builtin_inff() ? 0u : float_key(f); }
+  // -inf (key 0x007FFFFF) and the negative NaNs below it (keys < 2^23) are not
+  // candidates: key 0.  ((k >> 23) - 1 is negative exactly for those keys.)
+  __device__ __forceinline__ uint32_t key(float f, int rel) const {
+    const uint32_t k = order_key(f);
+    return k & below_mask(rel) & ~(uint32_t)((int32_t)((k >> 23) - 1u) >> 31);
+  }
   __device__ __forceinline__ int32_t token(int cell) const {
     return (cand[cell >> page_shift] << page_shift) + (cell & ((1 << page_shift) - 1));
   }
 };
 
-// Top-k of one row by one workgroup of NT threads: `row` holds n cells (n <= NT*EPT), the
-// k selected token indices go to out[0..k); when the row has at most k valid cells, all
-// of them are output, then -1 (DenseRow: 0..n-1).  Ties go to the earlier cell.  Every
-// thread of the block calls it with the same arguments.
-template <int NT, int EPT, class Map = DenseRow>
-__device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
-                                         TopkShared<NT, EPT>& sh, const Map map = Map()) {
+// The exact path for a row whose boundary bucket holds more keys than the ranking list
+// (long runs of equal values).  It re-reads the row's cells (from cache) in rolled loops
+// instead of taking the caller's register keys, so it holds no per-round state and the
+// common path's register allocation does not carry it.  Two more histogram passes over the keys inside digit d1 fix K*, the
+// k-th largest key; then cells > K* and the first need_eq cells == K* in index order are
+// output, their slots from per-(round, wave) ballot counts: cell i = e*NT + wave*64 + lane,
+// so (e, wave) pairs in row-major order are index order.
+template <int NT, int EPT, class Map>
+__device__ __forceinline__ void topk_row_exact(const float* __restrict__ row, int n, int k,
+                                                         int32_t* __restrict__ out, TopkShared<NT, EPT>* shp,
+                                                         const Map map, uint32_t d1, int kk, int ne) {
   using C = Cfg<NT>;
   constexpr int NW = NT / 64;
+  TopkShared<NT, EPT>& sh = *shp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (n <= (Map::kCountValid ? 0 : k)) {  // uniform
-    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? map.token(i) : -1;
-    return;
-  }
-  const int ne = (n + NT - 1) / NT;  // rounds that hold valid cells (uniform)
-  // Branch-free loads at an in-bounds index (cells past n read cell n-1 and are masked),
-  // so all loads are in flight together; the histogram is cleared while they are.
-  float raw[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) raw[e] = row[min(e * NT + tid, n - 1)];
-  for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
-  uint32_t key[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) key[e] = (e * NT + tid < n) ? map.key(raw[e]) : 0u;
-  if constexpr (Map::kCountValid) {
-    // At most k valid cells: all of them, in cell order, then -1.  (The scan's barrier
-    // also orders the histogram clear; wave_tot is next written after pass 1's barrier.)
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) cnt += key[e] != 0u ? 1 : 0;
-    int total;
-    int pos = block_excl_scan<NT>(cnt, sh.wave_tot, total);
-    if (total <= k) {  // uniform
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if (key[e] != 0u) out[pos++] = map.token(e * NT + tid);
-      for (int i = total + tid; i < k; i += NT) out[i] = -1;
-      return;
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 1: the top D1 bits of every valid cell ----
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (e < ne && key[e] != 0u) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
-  __syncthreads();
-  select_digit<NT, C::Bins>(sh, k);
-  const uint32_t d1 = (uint32_t)sh.sel_digit;
-  int kk = k - sh.sel_above;
-
-  // ---- cells above the bucket, and the bucket itself (one block scan of two counts) ----
-  // Cells past n (key 0) can only fall in the bucket when d1 == 0; they then rank below
-  // every valid candidate, and the histogram (valid cells only) needs fewer than those.
-  int n_gt = 0, n_in = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const uint32_t dg = key[e] >> C::Shift;
-    n_gt += dg > d1 ? 1 : 0;
-    n_in += dg == d1 ? 1 : 0;
-  }
-  int tot_gt, nc, pos_gt, pos_in;
-  block_excl_scan2<NT>(n_gt, n_in, sh.wave_tot, pos_gt, pos_in, tot_gt, nc);
-  if (nc <= kRankCap) {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if ((key[e] >> C::Shift) == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
-    __syncthreads();
-    // Rank of each candidate among the bucket by (key desc, index asc); composites are
-    // distinct, so the ranks are a permutation of 0..nc-1.  G adjacent lanes share one
-    // candidate (G = NT / nc rounded to a power of two, at most 64), each counting a
-    // strided part of the list, and a lane-xor reduction sums their counts.
-    int np2 = 1;
-    while (np2 < nc) np2 <<= 1;
-    const int G = max(1, min(64, NT / np2));
-    const int per_sweep = NT / G;
-    for (int base = 0; base < nc; base += per_sweep) {
-      const int c = base + tid / G, part = tid & (G - 1);
-      const uint64_t me = sh.cand[min(c, nc - 1)];
-      int cnt = 0;
-      if (c < nc) {
-        int t = part;
-        for (; t + 7 * G < nc; t += 8 * G) {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) cnt += sh.cand[t + u * G] > me ? 1 : 0;
-        }
-        for (; t < nc; t += G) cnt += sh.cand[t] > me ? 1 : 0;
-      }
-      for (int m = 1; m < G; m <<= 1) cnt += shfl_xor(cnt, m);
-      if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = map.token((int)~(uint32_t)me);
-    }
-    // cells above the bucket: after the barriers, so no store is waited for
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
-    return;
-  }
-
-  // ---- large bucket: fallback passes A and B over the register keys fix K* ----
+  auto key_at = [&](int e) { return map.key(row[min(e * NT + tid, n - 1)], e * NT + tid - n); };
   uint32_t prefix = d1 << C::Shift, pmask = ~0u << C::Shift;
-#pragma unroll
+#pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? C::Shift - C::FbBitsA : 0;
     const uint32_t dmask = pass == 0 ? (1u << C::FbBitsA) - 1u : (1u << C::FbBitsB) - 1u;
     for (int i = tid; i < kFbBins; i += NT) sh.hist[i] = 0;
     __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if (e < ne && key[e] != 0u && (key[e] & pmask) == prefix)
-        atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1u);
+#pragma unroll 1
+    for (int e = 0; e < ne; ++e) {
+      const uint32_t kv = key_at(e);
+      if (kv != 0u && (kv & pmask) == prefix) atomicAdd(&sh.hist[(kv >> shift) & dmask], 1u);
+    }
     __syncthreads();
     select_digit<NT, kFbBins>(sh, kk);
     prefix |= (uint32_t)sh.sel_digit << shift;
@@ -272,14 +241,12 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   }
   const uint32_t kstar = prefix;
   const int need_eq = kk;  // how many cells equal to K* are taken (>= 1)
-
-  // ---- ranks in index order: per (round e, wave) counts of >K* and ==K* cells ----
-  // Cell i = e*NT + wave*64 + lane, so (e, wave) pairs in row-major order are index order.
   constexpr int NE = EPT * NW;
-#pragma unroll
+#pragma unroll 1
   for (int e = 0; e < EPT; ++e) {  // kstar >= 1, so cells past n (key 0) never count
-    const uint64_t bg = __ballot(key[e] > kstar);
-    const uint64_t be = __ballot(key[e] == kstar);
+    const uint32_t kv = e < ne ? key_at(e) : 0u;
+    const uint64_t bg = __ballot(kv > kstar);
+    const uint64_t be = __ballot(kv == kstar);
     if (lane == 0) {
       sh.cnt_gt[e * NW + wave] = __popcll(bg);
       sh.cnt_eq[e * NW + wave] = __popcll(be);
@@ -311,20 +278,119 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   }
   __syncthreads();
   const uint64_t lt = lanemask_lt(lane);
+#pragma unroll 1
+  for (int e = 0; e < ne; ++e) {
+    const uint32_t kv = key_at(e);
+    const bool is_gt = kv > kstar;
+    const bool is_eq = kv == kstar;
+    const uint64_t bg = __ballot(is_gt);
+    const uint64_t be = __ballot(is_eq);
+    const int gt_before = sh.cnt_gt[e * NW + wave] + __popcll(bg & lt);
+    const int eq_before = sh.cnt_eq[e * NW + wave] + __popcll(be & lt);
+    const int pos = gt_before + min(eq_before, need_eq);
+    if ((is_gt || (is_eq && eq_before < need_eq)) && pos < k) out[pos] = map.token(e * NT + tid);
+  }
+}
+
+// Top-k of one row by one workgroup of NT threads: `row` holds n cells (n <= NT*EPT), the
+// k selected token indices go to out[0..k); when the row has at most k valid cells, all
+// of them are output, then -1 (DenseRow: 0..n-1).  Ties go to the earlier cell.  Every
+// thread of the block calls it with the same arguments.
+template <int NT, int EPT, class Map = DenseRow>
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
+                                         TopkShared<NT, EPT>& sh, const Map map = Map()) {
+  using C = Cfg<NT>;
+  const int tid = threadIdx.x;
+  if (n <= (Map::kCountValid ? 0 : k)) {  // uniform
+    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? map.token(i) : -1;
+    return;
+  }
+  const int ne = __builtin_amdgcn_readfirstlane((n + NT - 1) / NT);  // rounds holding valid cells; <= EPT
+  // Branch-free loads at an in-bounds index (cells past n read cell n-1, a cache hit, and are
+  // masked to key 0), all in flight together; the histogram is cleared while they are.  The
+  // phases after this skip every group of 8 rounds wholly past n (for_rounds), which is
+  // most of a short row's rounds.
+  float raw[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    if (e < ne) {
-      const int i = e * NT + tid;
-      const bool is_gt = key[e] > kstar;
-      const bool is_eq = key[e] == kstar;
-      const uint64_t bg = __ballot(is_gt);
-      const uint64_t be = __ballot(is_eq);
-      const int gt_before = sh.cnt_gt[e * NW + wave] + __popcll(bg & lt);
-      const int eq_before = sh.cnt_eq[e * NW + wave] + __popcll(be & lt);
-      const int pos = gt_before + min(eq_before, need_eq);
-      if ((is_gt || (is_eq && eq_before < need_eq)) && pos < k) out[pos] = map.token(i);
+  for (int e = 0; e < EPT; ++e) raw[e] = row[(uint32_t)min(e * NT + tid, n - 1)];
+  for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
+  uint32_t key[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) key[e] = map.key(raw[e], e * NT + tid - n);
+  if constexpr (Map::kCountValid) {
+    // At most k valid cells: all of them, in cell order, then -1.  (The scan's barrier
+    // also orders the histogram clear; wave_tot is next written after pass 1's barrier.)
+    int cnt = 0;
+    for_rounds<EPT>(ne, [&](int e) { cnt += key[e] != 0u ? 1 : 0; });
+    int total;
+    int pos = block_excl_scan<NT>(cnt, sh.wave_tot, total);
+    if (total <= k) {  // uniform
+      for_rounds<EPT>(ne, [&](int e) {
+        if (key[e] != 0u) out[pos++] = map.token(e * NT + tid);
+      });
+      for (int i = total + tid; i < k; i += NT) out[i] = -1;
+      return;
     }
   }
+  __syncthreads();
+
+  // ---- pass 1: the top D1 bits of every valid cell ----
+  for_rounds<EPT>(ne, [&](int e) {
+    if (key[e] != 0u) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
+  });
+  __syncthreads();
+  select_digit<NT, C::Bins>(sh, k);
+  const uint32_t d1 = (uint32_t)sh.sel_digit;
+  int kk = k - sh.sel_above;
+
+  // ---- cells above the bucket, and the bucket itself (one block scan of two counts) ----
+  // Cells past n (key 0) can only fall in the bucket when d1 == 0; they then rank below
+  // every valid candidate, and the histogram (valid cells only) needs fewer than those.
+  int n_gt = 0, n_in = 0;
+  for_rounds<EPT>(ne, [&](int e) {
+    const uint32_t dg = key[e] >> C::Shift;
+    n_gt += dg > d1 ? 1 : 0;
+    n_in += dg == d1 ? 1 : 0;
+  });
+  int tot_gt, nc, pos_gt, pos_in;
+  block_excl_scan2<NT>(n_gt, n_in, sh.wave_tot, pos_gt, pos_in, tot_gt, nc);
+  if (nc <= kRankCap) {
+    for_rounds<EPT>(ne, [&](int e) {
+      if ((key[e] >> C::Shift) == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
+    });
+    __syncthreads();
+    // Rank of each candidate among the bucket by (key desc, index asc); composites are
+    // distinct, so the ranks are a permutation of 0..nc-1.  G adjacent lanes share one
+    // candidate (G = NT / nc rounded to a power of two, at most 64), each counting a
+    // strided part of the list, and a lane-xor reduction sums their counts.
+    int np2 = 1;
+    while (np2 < nc) np2 <<= 1;
+    const int G = max(1, min(64, NT / np2));
+    const int per_sweep = NT / G;
+    for (int base = 0; base < nc; base += per_sweep) {
+      const int c = base + tid / G, part = tid & (G - 1);
+      const uint64_t me = sh.cand[min(c, nc - 1)];
+      int cnt = 0;
+      if (c < nc) {
+        int t = part;
+        for (; t + 7 * G < nc; t += 8 * G) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cnt += sh.cand[t + u * G] > me ? 1 : 0;
+        }
+        for (; t < nc; t += G) cnt += sh.cand[t] > me ? 1 : 0;
+      }
+      for (int m = 1; m < G; m <<= 1) cnt += shfl_xor(cnt, m);
+      if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = map.token((int)~(uint32_t)me);
+    }
+    // cells above the bucket: after the barriers, so no store is waited for
+    for_rounds<EPT>(ne, [&](int e) {
+      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
+    });
+    return;
+  }
+
+  // ---- large bucket (long runs of equal values): the exact path ----
+  topk_row_exact<NT, EPT, Map>(row, n, k, out, &sh, map, d1, kk, ne);
 }
 
 }  // namespace idx
