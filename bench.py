@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="report the eager step time as the value (default: HIP-graph replay of the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="the one workload named by --config/--kv, not the whole set")
     ap.add_argument("--separate", action="store_true",
                     help="time the step as three calls even where the fused decode step applies")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
@@ -216,10 +217,20 @@ def summarize(dirs, traffic_key=None, calib_mib=0):
         fh.write("\n")
 
 
-def cpu_baseline(W, fmt, budget_s):
-    """The oracle, as it stands, on the host cores: one full step (K store of the new
-    rows, logits of every row, top-k of every row) for the decode workloads; for the
-    prefill workload a bounded sample of rows, scaled to one step."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, fmt, budget_s, max_rows=4096):
+    """The oracle, as it stands, on the host cores: one step (K store of the new rows,
+    logits and top-k of the rows) over every row when there are at most max_rows, else
+    over a seeded sample of rows (256, or max_rows if fewer), scaled to the whole step."""
     import oracle
     pt = W.page_table
     pids = np.unique(pt[pt >= 0]).astype(np.int64)
@@ -238,11 +249,11 @@ def cpu_baseline(W, fmt, budget_s):
         q, w = oracle.q_quant_fp8(W.q_rows, W.w)
         qs = None
     rows_all = np.arange(W.rows, dtype=np.int64)
-    if W.rows <= 4096:
+    if W.rows <= max_rows:
         sample_rows = rows_all
     else:
         rng = np.random.default_rng(7)
-        sample_rows = np.sort(rng.choice(W.rows, 256, replace=False)).astype(np.int64)
+        sample_rows = np.sort(rng.choice(W.rows, min(256, max_rows), replace=False)).astype(np.int64)
     new = step_rows(W)
     times = []
     t_end = time.perf_counter() + budget_s
@@ -259,111 +270,24 @@ def cpu_baseline(W, fmt, budget_s):
     per_step = float(np.median(times)) * (W.rows / sample_rows.size)
     sample = (f"{len(times)} oracle step(s): K store of {len(new)} rows + logits and top-k of "
               f"{sample_rows.size}/{W.rows} rows" + ("" if sample_rows.size == W.rows else ", scaled to all rows"))
-    return {"value": per_step * 1e6, "unit": "us/call", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": sample}
+    return {"value": round(per_step * 1e6, 1), "unit": "us/call", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": sample, "cpu": cpu_model(), "nproc": os.cpu_count()}
 
 
-def main():
-    args = parse()
-    if args.summarize:
-        summarize(args.summarize, args.traffic_key, args.calib_mib)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
-        sys.exit(2)
-    import torch
-    from sparse_attention_indexer_idx_amd import binding as bd
-    from sparse_attention_indexer_idx_amd import workloads as wl
+def scorer_kernel(W):
+    """The scorer form idx_logits_paged takes for this shape (mirrors its routing)."""
+    ht = (W.H + 15) // 16
+    stream_ok = W.n_q <= 4 and W.B <= 1024 and W.max_ctx <= (1 << 30) and W.B * ((W.max_ctx + 63) // 64) < (1 << 31)
+    if stream_ok and W.n_q > 1 and W.n_q * ht > 4:
+        return "logits_stream_kernel"
+    if stream_ok and W.n_q == 1 and W.B * W.max_ctx >= (1 << 21):
+        return "logits_stream_kernel"
+    if W.n_q * ht <= 16:
+        return "logits_decode_rows_kernel" if (W.n_q > 1 and W.n_q * ht > 4) else "logits_decode_kernel"
+    return "logits_prefill_kernel"
 
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
-    bd.load()
-    if bd.idx_device_check() != bd.IDX_OK:
-        raise SystemExit("device is not gfx950")
-    fmt = 0 if args.kv == "mxfp4" else 1
-    W = wl.make_workload(args.config, kv_format=fmt, scale={"H": args.heads} if args.heads else None)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
-    P = W.page_size
-    page_bytes = (68 if fmt == 0 else 132) * P
-    stride = max(W.page_stride_bytes, page_bytes)
-    pool_bytes = W.offset_bytes + W.num_pages * stride
-    used_bytes = int(np.minimum(W.ctx, W.max_ctx).sum()) * (68 if fmt == 0 else 132)
-    # Prefill re-reads its small K from L2 by design and writes far more logits than
-    # the last-level cache holds, so only decode rotates pool replicas.
-    prefill_like = not decode_form(W)
-    replicas = 1 if (args.warm or prefill_like) else max(2, int(np.ceil(2 * LLC_BYTES / max(used_bytes, 1))) + 1)
-    replicas = min(replicas, 64, max(1, int((64 << 30) // pool_bytes)))
 
-    # ---- inputs in HBM ----
-    k_all = dev(W.k_rows.view(np.int16)).view(torch.bfloat16)
-    gamma, cos_sin = dev(W.gamma), dev(W.cos_sin)
-    positions, slots = dev(W.positions), dev(W.slots)
-    pools = []
-    for _ in range(replicas):
-        t = torch.empty((pool_bytes + 256,), dtype=torch.uint8, device="cuda")
-        shift = (-t.data_ptr()) % 256
-        pools.append((t, bd.make_pool(t[shift:], W.offset_bytes, stride, W.num_pages, P, fmt)))
-    store = bd.idx_k_store_mxfp4 if fmt == 0 else bd.idx_k_store_fp8
-    for _, pv in pools:  # fill every replica's cache with the whole context (setup)
-        store(pv, k_all, gamma, W.eps, positions, cos_sin, slots)
-    q_bf16 = dev(W.q_rows.reshape(-1, 128).view(np.int16)).view(torch.bfloat16)
-    nvec = q_bf16.shape[0]
-    if fmt == 0:
-        q = torch.empty((nvec, 64), dtype=torch.uint8, device="cuda")
-        qs = torch.empty((nvec, 4), dtype=torch.uint8, device="cuda")
-        bd.idx_q_quant_mxfp4(q_bf16, q, qs)
-        w = dev(W.w.reshape(-1))
-    else:
-        q = torch.empty((nvec, 128), dtype=torch.uint8, device="cuda")
-        qs = None
-        w = torch.empty((nvec,), dtype=torch.float32, device="cuda")
-        bd.idx_q_quant_fp8(q_bf16, dev(W.w.reshape(-1)), q, w)
-    pt, ctx = dev(W.page_table), dev(W.ctx)
-    logits = torch.empty((W.rows, W.max_ctx), dtype=torch.float32, device="cuda")
-    out = torch.empty((W.rows, W.topk), dtype=torch.int32, device="cuda")
-    new = step_rows(W)
-    k_new, pos_new, slot_new = k_all[dev(new)], positions[dev(new)], slots[dev(new)]
-    if args.calib_copy_mib:  # a plain device copy of known size, outside the timed region
-        src = torch.ones((args.calib_copy_mib << 20,), dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        del src, dst
-    torch.cuda.synchronize()
-
-    def k_store(i):
-        store(pools[i % replicas][1], k_new, gamma, W.eps, pos_new, cos_sin, slot_new)
-
-    def score(i):
-        bd.idx_logits_paged(pools[i % replicas][1], q, qs, w, pt, ctx, W.B, W.n_q, W.H, W.max_ctx, logits)
-
-    def topk(i):
-        bd.idx_topk(logits, ctx, W.B, W.n_q, W.topk, out)
-
-    def step(i):
-        k_store(i)
-        score(i)
-        topk(i)
-
-    ws = torch.zeros((max(bd.idx_workspace_bytes(W.B, W.n_q, W.H, W.max_ctx, W.topk), 256) // 4,), dtype=torch.int32,
-                     device="cuda")
-
-    def fused_step(i):
-        bd.idx_decode_step(pools[i % replicas][1], k_new, gamma, W.eps, pos_new, cos_sin, slot_new, q, qs, w, pt, ctx,
-                           W.B, W.n_q, W.H, W.max_ctx, logits, W.topk, out, ws)
-
-    # the step through idx_decode_step when it runs as the one fused kernel there
-    fused = not args.separate and len(new) == W.B * W.n_q
-    if fused:
-        try:
-            fused = bd.idx_decode_step_fused(W.B, W.n_q, W.H, W.max_ctx) == 1
-        except bd.IdxError as e:
-            if e.status != bd.IDX_EUNSUPPORTED:
-                raise
-            fused = False
-    if fused:
-        fused_step(0)
-        torch.cuda.synchronize()
-
+def make_held(torch):
     def held(fn, n, host_s):
         """GPU time of n back-to-back calls fn(0..n-1): a spin kernel holds the GPU while
         the host enqueues them, and one event pair brackets the whole run, so neither
@@ -382,33 +306,270 @@ def main():
         per = [ev[gi].elapsed_time(ev[gi + 1]) * 1e3 / ((gi + 1) * n // groups - gi * n // groups)
                for gi in range(groups)]
         return ev[0].elapsed_time(ev[-1]) * 1e3 / n, np.array(per)
+    return held
+
+
+def time_graph(torch, step_fn, L, steps):
+    """GPU time per step of `steps` steps replayed from HIP graphs: graph A holds L
+    consecutive steps (L a multiple of the replica count, at least 8, so a replay's fixed
+    launch cost is shared as it is across the layers of a captured model), graph B the
+    steps mod L remaining ones, so the timed region is exactly `steps` steps; and the host
+    wall time of the same steps enqueued as the host goes (ms per step, both)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(L):
+            step_fn(i)  # warm the captured configuration eagerly on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step_fn(i)
+        return g
+    graph_a = capture(L)
+    rem = steps % L
+    graph_b = capture(rem) if rem else None
+
+    def replay_k():
+        for _ in range(steps // L):
+            graph_a.replay()
+        if graph_b is not None:
+            graph_b.replay()
+    replay_k()  # warm-up replays (untimed)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    replay_k()
+    host_s = (time.perf_counter() - h0) / steps
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int((2.0 * host_s * steps + 2e-3) * 2.4e9))
+    g0.record()
+    replay_k()
+    g1.record()
+    torch.cuda.synchronize()
+    gpu_ms = g0.elapsed_time(g1) / steps
+    t0 = time.perf_counter()
+    replay_k()
+    torch.cuda.synchronize()
+    return gpu_ms, (time.perf_counter() - t0) * 1e3 / steps
+
+
+class Run:
+    """Device inputs of one workload, resident in HBM: pool replicas holding the whole
+    context (rotated so that each step reads K from HBM rather than the last-level cache),
+    packed Q and weights, page table, lengths, output buffers and the step's new rows."""
+
+    def __init__(self, torch, bd, wl, config, kv, warm=False, heads=0, calib_copy_mib=0):
+        self.torch, self.bd = torch, bd
+        self.config, self.kv = config, kv
+        fmt = self.fmt = 0 if kv == "mxfp4" else 1
+        W = self.W = wl.make_workload(config, kv_format=fmt, scale={"H": heads} if heads else None)
+        dev = self.dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        P = W.page_size
+        page_bytes = (68 if fmt == 0 else 132) * P
+        stride = max(W.page_stride_bytes, page_bytes)
+        pool_bytes = W.offset_bytes + W.num_pages * stride
+        used_bytes = int(np.minimum(W.ctx, W.max_ctx).sum()) * (68 if fmt == 0 else 132)
+        # Prefill re-reads its small K from L2 by design and writes far more logits than
+        # the last-level cache holds, so only decode rotates pool replicas.
+        self.prefill = not decode_form(W)
+        replicas = 1 if (warm or self.prefill) else max(2, int(np.ceil(2 * LLC_BYTES / max(used_bytes, 1))) + 1)
+        self.replicas = min(replicas, 64, max(1, int((64 << 30) // pool_bytes)))
+        self.cache = "warm" if warm else f"cold ({self.replicas} pool replicas rotated)"
+        k_all = dev(W.k_rows.view(np.int16)).view(torch.bfloat16)
+        self.gamma, self.cos_sin = dev(W.gamma), dev(W.cos_sin)
+        positions, slots = dev(W.positions), dev(W.slots)
+        self.pools = []
+        for _ in range(self.replicas):
+            t = torch.empty((pool_bytes + 256,), dtype=torch.uint8, device="cuda")
+            shift = (-t.data_ptr()) % 256
+            self.pools.append((t, bd.make_pool(t[shift:], W.offset_bytes, stride, W.num_pages, P, fmt)))
+        self.store = bd.idx_k_store_mxfp4 if fmt == 0 else bd.idx_k_store_fp8
+        for _, pv in self.pools:  # fill every replica's cache with the whole context (setup)
+            self.store(pv, k_all, self.gamma, W.eps, positions, self.cos_sin, slots)
+        self.q_bf16 = dev(W.q_rows.reshape(-1, 128).view(np.int16)).view(torch.bfloat16)
+        nvec = self.q_bf16.shape[0]
+        if fmt == 0:
+            self.q = torch.empty((nvec, 64), dtype=torch.uint8, device="cuda")
+            self.qs = torch.empty((nvec, 4), dtype=torch.uint8, device="cuda")
+            bd.idx_q_quant_mxfp4(self.q_bf16, self.q, self.qs)
+            self.w = dev(W.w.reshape(-1))
+        else:
+            self.q = torch.empty((nvec, 128), dtype=torch.uint8, device="cuda")
+            self.qs = None
+            self.w = torch.empty((nvec,), dtype=torch.float32, device="cuda")
+            bd.idx_q_quant_fp8(self.q_bf16, dev(W.w.reshape(-1)), self.q, self.w)
+        self.pt, self.ctx = dev(W.page_table), dev(W.ctx)
+        self.logits = torch.empty((W.rows, W.max_ctx), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((W.rows, W.topk), dtype=torch.int32, device="cuda")
+        self.new = step_rows(W)
+        nd = dev(self.new)
+        self.k_new, self.pos_new, self.slot_new = k_all[nd], positions[nd], slots[nd]
+        del k_all, positions, slots
+        self.ws = torch.zeros((max(bd.idx_workspace_bytes(W.B, W.n_q, W.H, W.max_ctx, W.topk), 256) // 4,),
+                              dtype=torch.int32, device="cuda")
+        if calib_copy_mib:  # a plain device copy of known size, outside the timed region
+            src = torch.ones((calib_copy_mib << 20,), dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            del src, dst
+        torch.cuda.synchronize()
+
+    def pool(self, i):
+        return self.pools[i % self.replicas][1]
+
+    def k_store(self, i):
+        W = self.W
+        self.store(self.pool(i), self.k_new, self.gamma, W.eps, self.pos_new, self.cos_sin, self.slot_new)
+
+    def score(self, i):
+        W = self.W
+        self.bd.idx_logits_paged(self.pool(i), self.q, self.qs, self.w, self.pt, self.ctx, W.B, W.n_q, W.H,
+                                 W.max_ctx, self.logits)
+
+    def topk(self, i):
+        W = self.W
+        self.bd.idx_topk(self.logits, self.ctx, W.B, W.n_q, W.topk, self.out)
+
+    def step(self, i):
+        self.k_store(i)
+        self.score(i)
+        self.topk(i)
+
+    def fused_step(self, i):
+        W = self.W
+        self.bd.idx_decode_step(self.pool(i), self.k_new, self.gamma, W.eps, self.pos_new, self.cos_sin,
+                                self.slot_new, self.q, self.qs, self.w, self.pt, self.ctx, W.B, W.n_q, W.H, W.max_ctx,
+                                self.logits, W.topk, self.out, self.ws)
+
+    def fuses(self):
+        """Whether idx_decode_step runs this step as its one fused kernel."""
+        W = self.W
+        if len(self.new) != W.B * W.n_q:
+            return False
+        try:
+            return self.bd.idx_decode_step_fused(W.B, W.n_q, W.H, W.max_ctx) == 1
+        except self.bd.IdxError as e:
+            if e.status != self.bd.IDX_EUNSUPPORTED:
+                raise
+            return False
+
+
+def scorer_roof(R, ab, s_mean):
+    """Roofline of the scorer: algorithmic bytes (decode forms, against HBM) or FP4 / FP8
+    flops (prefill form, against the MFMA peak of its format) over its mean duration."""
+    W, fmt = R.W, R.fmt
+    shash = scorer_source_hash()
+    if R.prefill:
+        achieved = ab["flops"] / (s_mean * 1e-6) / 1e12
+        peak = FP4_PEAK_TFLOPS if fmt == 0 else FP8_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "algorithmic_flops": ab["flops"]}
+    else:
+        achieved = ab["scorer"] / (s_mean * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = scorer_kernel(W)
+    roof["traffic"] = traffic_from_profiles(f"cfg{R.config}_{R.kv}", shash)
+    roof["algorithmic_bytes"] = ab["scorer"]
+    roof["source_hash"] = shash
+    return roof
+
+
+def summary(R, held, steps, cpu_budget_s, with_cpu):
+    """One workload measured the short way: each kernel alone back to back, the step
+    replayed from HIP graphs, the scorer's and the top-k's rooflines, and the oracle on a
+    bounded sample of rows."""
+    W = R.W
+    for i in range(3):
+        R.step(i)
+    R.torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(3):
+        R.step(i)
+    host_s = (time.perf_counter() - h0) / 3
+    k_mean, _ = held(R.k_store, steps, host_s)
+    s_mean, _ = held(R.score, steps, host_s)
+    t_mean, _ = held(R.topk, steps, host_s)
+    fused = R.fuses()
+    L = R.replicas * max(1, -(-8 // R.replicas))
+    graph_ms, _ = time_graph(R.torch, R.fused_step if fused else R.step, L, steps)
+    ab = algorithmic_bytes(W, R.fmt, len(R.new))
+    tk_gbs = ab["topk"] / (t_mean * 1e-6) / 1e9
+    d = {"workload": W.name, "kv": R.kv, "B": W.B, "n_q": W.n_q, "H": W.H, "page_size": W.page_size,
+         "max_ctx": W.max_ctx, "topk": W.topk, "cache": R.cache,
+         "step_us": round(graph_ms * 1e3, 3),
+         "path": "fused idx_decode_step" if fused else "idx_k_store + idx_logits_paged + idx_topk",
+         "k_store_us": round(k_mean, 3), "score_us": round(s_mean, 3), "topk_us": round(t_mean, 3),
+         "scorer_roofline": scorer_roof(R, ab, s_mean),
+         "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(tk_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["topk"],
+                           "kernel": "topk_kernel"}}
+    if with_cpu:
+        d["cpu_baseline"] = cpu_baseline(W, R.fmt, cpu_budget_s, max_rows=32)
+    return d
+
+
+# The five workloads a default run reports beside the headline one (config index, K format).
+ALL_CONFIGS = (("C0", 0, "mxfp4"), ("C1", 1, "mxfp4"), ("C2", 2, "mxfp4"), ("C3", 3, "mxfp4"),
+               ("C4a", 4, "mxfp4"), ("C4b", 4, "fp8"))
+
+
+def main():
+    args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.traffic_key, args.calib_mib)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+    from sparse_attention_indexer_idx_amd import binding as bd
+    from sparse_attention_indexer_idx_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    bd.load()
+    if bd.idx_device_check() != bd.IDX_OK:
+        raise SystemExit("device is not gfx950")
+    held = make_held(torch)
+    R = Run(torch, bd, wl, args.config, args.kv, warm=args.warm, heads=args.heads,
+            calib_copy_mib=args.calib_copy_mib)
+    W, fmt, P = R.W, R.fmt, R.W.page_size
+    fused = not args.separate and R.fuses()
+    if fused:
+        R.fused_step(0)
+        torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        step(i)
+        R.step(i)
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     for i in range(args.warmup):
-        step(i)
+        R.step(i)
     host_s = (time.perf_counter() - h0) / max(args.warmup, 1)  # host cost of enqueueing one step
     torch.cuda.synchronize()
     # Timed region: exactly K eager steps on the kernels' own (current) stream, then each
     # kernel alone K times back to back for its average duration.
-    eager_us, _ = held(step, args.steps, host_s)
+    eager_us, _ = held(R.step, args.steps, host_s)
     eager_ms = eager_us * 1e-3
-    k_mean, k_us = held(k_store, args.steps, host_s)
-    s_mean, s_us = held(score, args.steps, host_s)
-    t_mean, t_us = held(topk, args.steps, host_s)
+    k_mean, k_us = held(R.k_store, args.steps, host_s)
+    s_mean, s_us = held(R.score, args.steps, host_s)
+    t_mean, t_us = held(R.topk, args.steps, host_s)
     # the scorer on one pool replica over and over: K then sits in the last-level cache
-    w_mean, _ = held(lambda i: score(0), args.steps, host_s)
+    w_mean, _ = held(lambda i: R.score(0), args.steps, host_s)
     qprep_us = None
     if fmt == 0:
         # The Q-side preparation that feeds the scorer (rotation + MXFP4 packing + weight
         # fold of every query row's heads), timed alone; it is not part of the step.
-        q3 = q_bf16.view(W.rows, W.H, 128)
-        qpos = dev(np.array([max(W.valid_len(r) - 1, 0) for r in range(W.rows)], np.int32))
-        qp2, qs2 = torch.empty_like(q), torch.empty_like(qs)
-        w2 = torch.empty_like(w)
-        qprep_us, _ = held(lambda i: bd.idx_q_prep_mxfp4(q3, qpos, cos_sin, w, 0.0625, qp2, qs2, w2), args.steps,
+        q3 = R.q_bf16.view(W.rows, W.H, 128)
+        qpos = R.dev(np.array([max(W.valid_len(r) - 1, 0) for r in range(W.rows)], np.int32))
+        qp2, qs2 = torch.empty_like(R.q), torch.empty_like(R.qs)
+        w2 = torch.empty_like(R.w)
+        qprep_us, _ = held(lambda i: bd.idx_q_prep_mxfp4(q3, qpos, R.cos_sin, R.w, 0.0625, qp2, qs2, w2), args.steps,
                            host_s)
 
     cand_us = None
@@ -417,10 +578,10 @@ def main():
         # every row scores 16 blocks of its sequence drawn without replacement (seeded),
         # over the same rotated pool replicas; not part of the step.
         n_cand = min(16, W.page_table.shape[1])
-        cand = dev(wl.candidate_blocks(np.random.default_rng(77), W, n_cand))
+        cand = R.dev(wl.candidate_blocks(np.random.default_rng(77), W, n_cand))
         clog = torch.empty((W.rows, n_cand * P), dtype=torch.float32, device="cuda")
         cout = torch.empty((W.rows, W.topk), dtype=torch.int32, device="cuda")
-        cs_mean, _ = held(lambda i: bd.idx_logits_candidates(pools[i % replicas][1], q, qs, w, pt, ctx, W.B, W.n_q, W.H,
+        cs_mean, _ = held(lambda i: bd.idx_logits_candidates(R.pool(i), R.q, R.qs, R.w, R.pt, R.ctx, W.B, W.n_q, W.H,
                                                              cand, clog), args.steps, host_s)
         ct_mean, _ = held(lambda i: bd.idx_topk_candidates(clog, cand, P, W.B, W.n_q, W.topk, cout), args.steps,
                           host_s)
@@ -429,83 +590,19 @@ def main():
         cand_us = {"blocks_per_row": n_cand, "score": round(cs_mean, 3), "topk": round(ct_mean, 3),
                    "score_hbm_gbs": round(cbytes / (cs_mean * 1e-6) / 1e9, 1)}
 
-    # The step captured into HIP graphs, as a serving loop runs the indexer inside a
-    # captured forward pass: graph A holds L consecutive steps (L a multiple of the replica
-    # count, at least 8, so a replay's fixed launch cost is shared as it is across the
-    # layers of a captured model), graph B the K mod L remaining ones; the timed region is
-    # exactly K steps.
-    L = replicas * max(1, -(-8 // replicas))
-
-    def time_graph(step_fn):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(L):
-                step_fn(i)  # warm the captured configuration eagerly on the capture stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-
-        def capture(n):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(n):
-                    step_fn(i)
-            return g
-        graph_a = capture(L)
-        rem = args.steps % L
-        graph_b = capture(rem) if rem else None
-
-        def replay_k():
-            for _ in range(args.steps // L):
-                graph_a.replay()
-            if graph_b is not None:
-                graph_b.replay()
-        replay_k()  # warm-up replays (untimed)
-        torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        replay_k()
-        host_s = (time.perf_counter() - h0) / args.steps
-        torch.cuda.synchronize()
-        # GPU time of K steps (the host enqueues the replays while a spin kernel holds the
-        # GPU), and separately the wall time of K steps enqueued as the host goes.
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int((2.0 * host_s * args.steps + 2e-3) * 2.4e9))
-        g0.record()
-        replay_k()
-        g1.record()
-        torch.cuda.synchronize()
-        gpu_ms = g0.elapsed_time(g1) / args.steps
-        t0 = time.perf_counter()
-        replay_k()
-        torch.cuda.synchronize()
-        return gpu_ms, (time.perf_counter() - t0) * 1e3 / args.steps
-
-    graph_ms, graph_wall_ms = time_graph(step)
+    L = R.replicas * max(1, -(-8 // R.replicas))
+    graph_ms, graph_wall_ms = time_graph(torch, R.step, L, args.steps)
     sep_graph_ms = graph_ms
     fused_us = None
     if fused:
         # The same step through the fused entry point (K store + scorer + top-k in one
         # launch); its result equals the separate calls bit for bit (tested).
-        fused_us, _ = held(fused_step, args.steps, host_s)
-        graph_ms, graph_wall_ms = time_graph(fused_step)
+        fused_us, _ = held(R.fused_step, args.steps, host_s)
+        graph_ms, graph_wall_ms = time_graph(torch, R.fused_step, L, args.steps)
     ms_per_step = eager_ms if args.eager else graph_ms
 
-    ab = algorithmic_bytes(W, fmt, len(new))
-    shash = scorer_source_hash()
-    prefill = not decode_form(W)
-    if prefill:
-        achieved = ab["flops"] / (s_mean * 1e-6) / 1e12
-        peak = FP4_PEAK_TFLOPS if fmt == 0 else FP8_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    else:
-        achieved = ab["scorer"] / (s_mean * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = "logits_prefill_kernel" if prefill else "logits_decode_kernel"
-    roof["traffic"] = traffic_from_profiles(f"cfg{args.config}_{args.kv}", shash)
-    roof["algorithmic_bytes"] = ab["scorer"]
-    roof["source_hash"] = shash
+    ab = algorithmic_bytes(W, fmt, len(R.new))
+    roof = scorer_roof(R, ab, s_mean)
     fused_roof = None
     if fused_us is not None:
         fb = ab["scorer"] + ab["topk"] + ab["kstore"]
@@ -517,6 +614,7 @@ def main():
                       "note": "the whole step in one launch (K store + scorer + top-k), the top-k tail's "
                               "latency included"}
     step_us = ms_per_step * 1e3
+    tk_gbs = ab["topk"] / (t_mean * 1e-6) / 1e9
     result = {
         "metric": "indexer score+top-k us/call; HBM TB/s (decode), FP4 TFLOPS (prefill)",
         "value": round(step_us, 3),
@@ -529,8 +627,7 @@ def main():
         "dtype": "mxfp4" if fmt == 0 else "fp8_e4m3",
         "data": "synthetic (seeded N(0,1) bf16 K/Q rows, shuffled physical pages)",
         "config": {"workload": W.name, "B": W.B, "n_q": W.n_q, "H": W.H, "D": 128, "page_size": P,
-                   "max_ctx": W.max_ctx, "topk": W.topk, "kv": args.kv,
-                   "cache": "warm" if args.warm else f"cold ({replicas} pool replicas rotated)"},
+                   "max_ctx": W.max_ctx, "topk": W.topk, "kv": args.kv, "cache": R.cache},
         "step_us": {"graph": round(graph_ms * 1e3, 3), "eager": round(eager_ms * 1e3, 3),
                     "graph_wall": round(graph_wall_ms * 1e3, 3), "steps_per_graph": L,
                     "path": "fused idx_decode_step" if fused else "idx_k_store + idx_logits_paged + idx_topk",
@@ -547,18 +644,39 @@ def main():
         # scorer (the dominant one of the three); the scorer alone is always listed too
         "roofline": roof if fused_us is None else fused_roof,
         "scorer_roofline": roof,
+        "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(tk_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["topk"],
+                          "kernel": "topk_kernel"},
         "q_prep_us": None if qprep_us is None else round(qprep_us, 3),
         "candidates_us": cand_us,
-        "topk_hbm_gbs": round(ab["topk"] / (t_mean * 1e-6) / 1e9, 1),
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),
     }
-    result["device"] = device_rates(held, host_s)
+    result["device"] = device_rates(torch, held, host_s)
     result["qk_prep_fp8_us"] = qk_prep_fp8_times(held, host_s, args.steps)
     if not args.no_cpu_baseline:
         # the CPU leg: the oracle timed on the host cores, and the same-run precision
         # comparison against the oracle's unquantised scorer
         result["cpu_baseline"] = cpu_baseline(W, fmt, args.cpu_budget_s)
-        result["precision_vs_unquantized"] = precision_vs_unquantized(W, logits.cpu().numpy(), out.cpu().numpy())
+        result["precision_vs_unquantized"] = precision_vs_unquantized(W, R.logits.cpu().numpy(), R.out.cpu().numpy())
+    if not args.only:
+        # Every workload of the set, measured the short way (the headline one included,
+        # so the set reads as one table); each workload's buffers are freed before the next.
+        head = (args.config, args.kv)
+        del R
+        torch.cuda.empty_cache()
+        configs = {}
+        for name, cfg, kv in ALL_CONFIGS:
+            if args.warm or args.heads:
+                break
+            Rc = Run(torch, bd, wl, cfg, kv)
+            configs[name] = summary(Rc, held, min(args.steps, 50), 3.0, not args.no_cpu_baseline)
+            if (cfg, kv) != head and not args.no_cpu_baseline:
+                pr = precision_vs_unquantized(Rc.W, Rc.logits.cpu().numpy(), Rc.out.cpu().numpy(), n_rows=2)
+                configs[name]["precision_vs_unquantized"] = pr
+            del Rc
+            torch.cuda.empty_cache()
+            print(f"[bench] {name} done", file=sys.stderr, flush=True)
+        result["configs"] = configs
     print(json.dumps(result), flush=True)
 
 
@@ -626,22 +744,46 @@ def qk_prep_fp8_times(held, host_s, steps):
     return out
 
 
-def device_rates(held, host_s):
-    """CU count and peak clock as the runtime reports them, and the sustained rate of the
-    scaled 16x16x128 MFMA on register operands (idx_diag_mfma) next to the nominal peaks."""
-    import torch
+def device_rates(torch, held, host_s):
+    """CU count and peak clock as the runtime reports them; the sustained rate of the
+    scaled 16x16x128 MFMA on register operands (idx_diag_mfma) at 2, 4 and 8 waves per
+    SIMD, next to the nominal peaks; and the rate of a plain streaming read
+    (idx_diag_hbm_read) of the decode workload's K bytes (35,651,584) and of 1 GiB, each
+    the best over a few grid sizes, next to the nominal 8 TB/s."""
     from sparse_attention_indexer_idx_amd import binding as bd
     cus, khz = bd.idx_device_info()
-    blocks, rounds = 2048, 2000
-    buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    flops = blocks * 4 * rounds * 8 * 2 * 16 * 16 * 128
+    rounds = 2000
     rates = {}
     for name, f in (("fp4", 0), ("fp8", 1)):
-        bd.idx_diag_mfma(f, blocks, rounds, buf)
-        us, _ = held(lambda i: bd.idx_diag_mfma(f, blocks, rounds, buf), 5, host_s)
-        rates[name] = round(flops / (us * 1e-6) / 1e12, 1)
+        sweep = {}
+        for wps in (2, 4, 8):
+            blocks = cus * wps  # 4 waves per block, 4 SIMDs per CU
+            buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            bd.idx_diag_mfma(f, blocks, rounds, buf)
+            us, _ = held(lambda i: bd.idx_diag_mfma(f, blocks, rounds, buf), 5, host_s)
+            sweep[str(wps)] = round(blocks * 4 * rounds * 8 * 2 * 16 * 16 * 128 / (us * 1e-6) / 1e12, 1)
+            del buf
+        rates[name] = {"best": max(sweep.values()), "by_waves_per_simd": sweep}
+    reads = {}
+    for label, nbytes in (("decode_k_35.65MB", 35651584), ("1GiB", 1 << 30)):
+        # buffers rotated so that every read comes from HBM (their sum is twice the 256 MB
+        # last-level cache); one read = one launch over one buffer
+        nbuf = max(1, int(np.ceil(2 * LLC_BYTES / nbytes)) + 1) if nbytes < LLC_BYTES else 1
+        srcs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(nbuf)]
+        best = None
+        for blocks in (1024, 2048, 4096, 8192):
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            bd.idx_diag_hbm_read(srcs[0], blocks, out)
+            us, _ = held(lambda i: bd.idx_diag_hbm_read(srcs[i % nbuf], blocks, out), max(10, 2 * nbuf), host_s)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks, us)
+            del out
+        reads[label] = {"gbs": round(best[0], 1), "blocks": best[1], "us": round(best[2], 3), "buffers_rotated": nbuf}
+        del srcs
     return {"cus": cus, "clock_mhz": round(khz / 1000), "mfma_measured_tflops": rates,
-            "mfma_nominal_tflops": {"fp4": FP4_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS}}
+            "mfma_nominal_tflops": {"fp4": FP4_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS},
+            "hbm_read_measured": reads, "hbm_nominal_gbs": HBM_PEAK_GBS}
 
 
 if __name__ == "__main__":

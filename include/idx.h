@@ -392,6 +392,14 @@ int idx_diag_fp64(const double* a, const double* b, double* quot, double* root, 
  * so nothing is dead).  IDX_EINVAL for another fmt, blocks < 1, rounds < 0 or out NULL. */
 int idx_diag_mfma(int32_t fmt, int32_t blocks, int32_t rounds, float* out, void* stream);
 
+/* Diagnostic: a plain streaming read of `bytes` bytes at buf (device, 16-byte aligned,
+ * bytes a positive multiple of 16) by blocks x 256 threads, 16-byte non-temporal loads
+ * with eight in flight per thread and no arithmetic to speak of, so a caller timing it gets
+ * the HBM read rate a kernel can reach on this device next to the nominal 8 TB/s (and the
+ * rate for a transfer of a given size, start-up included).  out: device fp32
+ * [blocks * 256] (values meaningless).  IDX_EINVAL / IDX_EALIGN for bad arguments. */
+int idx_diag_hbm_read(const void* buf, int64_t bytes, int32_t blocks, float* out, void* stream);
+
 /* The current device's compute-unit count and peak shader clock (kHz), as the runtime
  * reports them.  IDX_EINVAL for a NULL pointer, IDX_EHIP when the runtime query fails. */
 int idx_device_info(int32_t* cus, int32_t* clock_khz);

@@ -20,7 +20,7 @@ IDX_KV_MXFP4, IDX_KV_FP8_E4M3 = 0, 1
 
 EXPORTS = ("idx_k_store_mxfp4", "idx_k_store_fp8", "idx_qk_prep_fp8", "idx_q_prep_mxfp4", "idx_q_quant_mxfp4", "idx_q_quant_fp8",
            "idx_logits_paged", "idx_logits_candidates", "idx_topk_candidates",
-           "idx_topk", "idx_workspace_bytes", "idx_decode_step", "idx_decode_step_noalloc", "idx_decode_step_fused", "idx_diag_fp64", "idx_diag_mfma",
+           "idx_topk", "idx_workspace_bytes", "idx_decode_step", "idx_decode_step_noalloc", "idx_decode_step_fused", "idx_diag_fp64", "idx_diag_mfma", "idx_diag_hbm_read",
            "idx_device_info", "idx_bytes_per_token", "idx_device_check", "idx_status_string")
 
 
@@ -72,6 +72,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                             V, V, ctypes.c_size_t, V],
         "idx_diag_fp64": [V, V, V, V, I64, V],
         "idx_diag_mfma": [I32, I32, I32, V, V],
+        "idx_diag_hbm_read": [V, I64, I32, V, V],
         "idx_device_info": [V, V],
         "idx_bytes_per_token": [I32],
         "idx_device_check": [],
@@ -235,6 +236,12 @@ def idx_diag_fp64(a, b, quot, root, stream=None):
 
 def idx_diag_mfma(fmt: int, blocks: int, rounds: int, out, stream=None):
     _check("idx_diag_mfma", load().idx_diag_mfma(fmt, blocks, rounds, _ptr(out), _stream(stream)))
+
+
+def idx_diag_hbm_read(buf, blocks: int, out, stream=None):
+    """Plain streaming read of the whole of `buf` (bytes a multiple of 16)."""
+    _check("idx_diag_hbm_read", load().idx_diag_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), blocks,
+                                                         _ptr(out), _stream(stream)))
 
 
 def idx_device_info() -> tuple[int, int]:

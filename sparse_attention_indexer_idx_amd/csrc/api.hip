@@ -486,6 +486,14 @@ IDX_EXPORT int idx_diag_mfma(int32_t fmt, int32_t blocks, int32_t rounds, float*
   return hip_status(idx::launch_diag_mfma(fmt, blocks, rounds, out, static_cast<hipStream_t>(stream)));
 }
 
+IDX_EXPORT int idx_diag_hbm_read(const void* buf, int64_t bytes, int32_t blocks, float* out, void* stream) {
+  if (!buf || !out || bytes < 16 || bytes % 16 != 0 || blocks < 1) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0) return IDX_EALIGN;
+  int st = check_device();
+  if (st != IDX_OK) return st;
+  return hip_status(idx::launch_diag_read(buf, bytes, blocks, out, static_cast<hipStream_t>(stream)));
+}
+
 IDX_EXPORT int idx_device_info(int32_t* cus, int32_t* clock_khz) {
   if (!cus || !clock_khz) return IDX_EINVAL;
   int dev = -1;

@@ -16,6 +16,11 @@ constexpr int kMfmaFmtFp8 = 0;  // OCP e4m3
 constexpr int kMfmaFmtFp4 = 4;  // E2M1
 constexpr uint32_t kE8m0One = 0x7F7F7F7Fu;  // every scale byte = 2^0
 
+// Fourth word of a raw buffer descriptor on the gfx9 family (gfx950 included): 32-bit
+// data format, no swizzle; with a zero stride, a load whose offset is at or past the
+// descriptor's byte count returns 0 instead of touching memory.
+constexpr int kBufferRsrcFlags = 0x00020000;
+
 __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
   return (double)__uint_as_float((uint32_t)h << 16);
 }

@@ -1,5 +1,6 @@
-// Diagnostic kernels: the sustained rate of the scaled 16x16x128 MFMA on register
-// operands (no memory traffic), which a measurement reports next to the nominal peak.
+// Diagnostic kernels, which a measurement reports next to the nominal peaks: the sustained
+// rate of the scaled 16x16x128 MFMA on register operands (no memory traffic), and the rate
+// of a plain streaming read (no compute) of a device buffer.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -30,7 +31,37 @@ __global__ __launch_bounds__(256) void diag_mfma_kernel(float* out, int rounds) 
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Plain streaming read: every thread reads 16-byte words at a grid stride, eight loads in
+// flight per iteration (non-temporal, as the scorer's K loads), and folds them into one
+// value it stores, so no load is dead.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void diag_read_kernel(const u32x4_t* __restrict__ buf, int64_t n16, float* out) {
+  constexpr int kUnroll = 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    u32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t v = __builtin_nontemporal_load(buf + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = (float)acc;
+}
+
 }  // namespace
+
+hipError_t launch_diag_read(const void* buf, int64_t bytes, int blocks, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(diag_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const u32x4_t*>(buf),
+                     bytes / 16, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_diag_mfma(int fmt, int blocks, int rounds, float* out, hipStream_t s) {
   if (fmt == 0)

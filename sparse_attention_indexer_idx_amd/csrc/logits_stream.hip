@@ -165,13 +165,115 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   }
 }
 
+// Several query rows (n_q = 2..4): a block is one worker; its four waves each fetch one of
+// a chunk's four K tiles into registers and then LDS, and wave j < n_q scores query row j
+// from all four tiles in LDS, so a chunk's K leaves HBM once per block.  Lane l of every
+// wave reads back the operand lane l fetched, which is its own MFMA operand for that tile.
+// Two LDS buffers alternate with one barrier per chunk; the next chunk's fetch is in
+// flight while the current one is scored.  The chunk loop runs over the longest row of
+// the sequence (row n_q - 1), the same for every wave; each row stores only its own cells.
+template <int FMT>
+struct alignas(16) StreamStage {
+  uint4 data[2][4][64][FMT == 0 ? 1 : 2];
+  uint32_t scale[2][4][64];
+};
+
+template <int FMT, int HT, int M>
+__global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
+  __shared__ StreamStage<FMT> st;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  int b, c0, c_end;
+  worker_run<M>(a, blockIdx.x, gridDim.x, lane, b, c0, c_end);
+  if (b < 0 || c0 >= c_end) return;  // block-uniform: no run for this worker
+  const int j = std::min(wave, a.n_q - 1);  // waves past n_q fetch but do not score
+  const bool scorer = wave < a.n_q;
+  const int64_t r = (int64_t)b * a.n_q + j;
+  const int P = a.pool.page_size, lgP = a.pool.page_shift;
+  const int last_page = (a.max_ctx - 1) >> lgP;
+  const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
+  const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);  // page ids are int32
+
+  v8i qa[HT];
+  uint32_t qs[HT];
+  v4f qw[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    load_q_tile<FMT>(a, r, ht, lane, qa[ht], qs[ht]);
+    qw[ht] = load_w_tile(a, r, ht, lane);
+  }
+  const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
+  const int n_r = valid_len(n_b, a.n_q, j);
+  const int n_end = std::min((n_b + 63) >> 6, c_end);  // the longest row's chunks in the run
+
+  auto page_of = [&](int cc, int t, bool& ok) {  // uniform
+    const int s0 = 64 * cc + 16 * t;
+    const int32_t pid = uniform(ptb[std::min(s0 >> lgP, last_page)]);
+    ok = pid >= 0 && pid < np32;
+    return pid;
+  };
+  // this wave's tile (t = wave) of chunk cc; past the run it reads page 0 row 0
+  auto fetch = [&](int cc) {
+    bool okk;
+    const int32_t pid = page_of(cc, wave, okk);
+    const bool use = okk && cc < n_end;
+    const uint8_t* page = a.pool.base + (use ? (int64_t)pid : 0) * a.pool.stride;
+    return load_k_tile<FMT, false>(page, P, use ? ((64 * cc + 16 * wave) & (P - 1)) : 0, lane);
+  };
+  auto stash = [&](int buf, const KTile<FMT>& k) {
+    st.data[buf][wave][lane][0] = make_uint4((uint32_t)k.v[0], (uint32_t)k.v[1], (uint32_t)k.v[2], (uint32_t)k.v[3]);
+    if (FMT == 1)
+      st.data[buf][wave][lane][FMT] = make_uint4((uint32_t)k.v[4], (uint32_t)k.v[5], (uint32_t)k.v[6], (uint32_t)k.v[7]);
+    st.scale[buf][wave][lane] = k.scale;
+  };
+  auto unstash = [&](int buf, int t) {
+    KTile<FMT> k;
+    const uint4 x = st.data[buf][t][lane][0];
+    if (FMT == 0) {
+      k.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+    } else {
+      const uint4 y = st.data[buf][t][lane][FMT];
+      k.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    }
+    k.scale = st.scale[buf][t][lane];
+    return k;
+  };
+  const float qnan = __builtin_nanf("");
+  float* __restrict__ out_row = a.logits + r * a.lstride;
+
+  KTile<FMT> nxt = fetch(c0);
+  for (int cc = c0; cc < n_end; ++cc) {  // block-uniform trip count
+    const int buf = (cc - c0) & 1;
+    stash(buf, nxt);
+    nxt = fetch(cc + 1);
+    __syncthreads();
+    if (scorer && 64 * cc < n_r) {  // uniform per wave
+      float p[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const KTile<FMT> kt = unstash(buf, t);
+        bool okt;
+        (void)page_of(cc, t, okt);
+        float acc = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc = relu_dot_acc(mfma<FMT>(qa[ht], qs[ht], kt), qw[ht], acc, ht == 0);
+        const float v = FMT == 1 ? acc * __uint_as_float(kt.scale) : acc;
+        p[t] = okt ? v : qnan;
+      }
+      const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
+      const int s = 64 * cc + lane;
+      if (s < n_r) out_row[s] = logit;
+    }
+  }
+}
+
 template <int FMT, int M>
 hipError_t launch_stream_m(const LogitsArgs& a, dim3 grid, int ht, hipStream_t s) {
   switch (ht) {
 #define IDX_STREAM_CASE(N) \
   case N: \
     if (a.n_q == 1) hipLaunchKernelGGL((logits_stream_kernel<FMT, N, true, M>), grid, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((logits_stream_kernel<FMT, N, false, M>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((logits_stream_rows_kernel<FMT, N, M>), grid, dim3(256), 0, s, a); \
     break;
     IDX_STREAM_CASE(1) IDX_STREAM_CASE(2) IDX_STREAM_CASE(3) IDX_STREAM_CASE(4)
     IDX_STREAM_CASE(5) IDX_STREAM_CASE(6) IDX_STREAM_CASE(7) IDX_STREAM_CASE(8)

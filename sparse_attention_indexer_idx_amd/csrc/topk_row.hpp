@@ -183,9 +183,8 @@ __device__ __forceinline__ void for_rounds(int ne, F&& f) {
 // key(f, rel): the key of cell value f, where rel = cell - n (negative inside the row).
 struct DenseRow {
   static constexpr bool kCountValid = false;
-  __device__ __forceinline__ uint32_t key(float f, int rel) const {
-    return max(order_key(f), 1u) & below_mask(rel);
-  }
+  __device__ __forceinline__ uint32_t key_full(float f) const { return max(order_key(f), 1u); }
+  __device__ __forceinline__ uint32_t key(float f, int rel) const { return key_full(f) & below_mask(rel); }
   __device__ __forceinline__ int32_t token(int cell) const { return cell; }
 };
 
@@ -195,10 +194,11 @@ struct CandidateRow {
   int32_t page_shift;
   // -inf (key 0x007FFFFF) and the negative NaNs below it (keys < 2^23) are not
   // candidates: key 0.  ((k >> 23) - 1 is negative exactly for those keys.)
-  __device__ __forceinline__ uint32_t key(float f, int rel) const {
+  __device__ __forceinline__ uint32_t key_full(float f) const {
     const uint32_t k = order_key(f);
-    return k & below_mask(rel) & ~(uint32_t)((int32_t)((k >> 23) - 1u) >> 31);
+    return k & ~(uint32_t)((int32_t)((k >> 23) - 1u) >> 31);
   }
+  __device__ __forceinline__ uint32_t key(float f, int rel) const { return key_full(f) & below_mask(rel); }
   __device__ __forceinline__ int32_t token(int cell) const {
     return (cand[cell >> page_shift] << page_shift) + (cell & ((1 << page_shift) - 1));
   }
@@ -306,17 +306,34 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
     return;
   }
   const int ne = __builtin_amdgcn_readfirstlane((n + NT - 1) / NT);  // rounds holding valid cells; <= EPT
-  // Branch-free loads at an in-bounds index (cells past n read cell n-1, a cache hit, and are
-  // masked to key 0), all in flight together; the histogram is cleared while they are.  The
-  // phases after this skip every group of 8 rounds wholly past n (for_rounds), which is
-  // most of a short row's rounds.
+  // Branch-free loads, all in flight together, through a buffer descriptor covering the
+  // row's n valid cells: the row base and the round's offset are scalar (so a load costs
+  // no vector address arithmetic), and a cell past n reads 0 (the descriptor's range
+  // check) and is masked to key 0.  The histogram is cleared while the loads are in flight.
+  // The phases after this skip every group of 8 rounds wholly past n (for_rounds), which
+  // is most of a short row's rounds.
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, n * 4, kBufferRsrcFlags);
   float raw[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) raw[e] = row[(uint32_t)min(e * NT + tid, n - 1)];
+  for (int e = 0; e < EPT; ++e)
+    raw[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, e * NT * 4, 0));
   for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
+  // Keys: only the group of rounds that holds the row's end needs the per-cell length mask;
+  // groups wholly inside the row take the unmasked key (a uniform branch per group keeps
+  // the masks from being computed ahead for every round and held in registers).
   uint32_t key[EPT];
+  constexpr int kGroup = EPT < 8 ? EPT : 8;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) key[e] = map.key(raw[e], e * NT + tid - n);
+  for (int g = 0; g < EPT; g += kGroup) {
+    if ((g + kGroup) * NT <= n) {
+#pragma unroll
+      for (int e = g; e < g + kGroup; ++e) key[e] = map.key_full(raw[e]);
+    } else {
+#pragma unroll
+      for (int e = g; e < g + kGroup; ++e) key[e] = map.key(raw[e], e * NT + tid - n);
+    }
+  }
   if constexpr (Map::kCountValid) {
     // At most k valid cells: all of them, in cell order, then -1.  (The scan's barrier
     // also orders the histogram clear; wave_tot is next written after pass 1's barrier.)
@@ -359,6 +376,11 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
       if ((key[e] >> C::Shift) == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
     });
     __syncthreads();
+    // Cells above the bucket: after the last barrier (so no barrier waits for these
+    // stores) and before the ranking (so the register keys are dead while it runs).
+    for_rounds<EPT>(ne, [&](int e) {
+      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
+    });
     // Rank of each candidate among the bucket by (key desc, index asc); composites are
     // distinct, so the ranks are a permutation of 0..nc-1.  G adjacent lanes share one
     // candidate (G = NT / nc rounded to a power of two, at most 64), each counting a
@@ -382,10 +404,6 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
       for (int m = 1; m < G; m <<= 1) cnt += shfl_xor(cnt, m);
       if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = map.token((int)~(uint32_t)me);
     }
-    // cells above the bucket: after the barriers, so no store is waited for
-    for_rounds<EPT>(ne, [&](int e) {
-      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
-    });
     return;
   }
 

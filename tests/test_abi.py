@@ -228,6 +228,16 @@ def test_valid_calls_report_missing_device(lib):
     assert lib.idx_device_check() == bd.IDX_EUNSUPPORTED
 
 
+def test_diag_read_checks(lib):
+    out = ctypes.c_void_p(FAKE)
+    assert lib.idx_diag_hbm_read(None, 1024, 4, out, None) == bd.IDX_EINVAL
+    assert lib.idx_diag_hbm_read(FAKE, 1000, 4, out, None) == bd.IDX_EINVAL      # not a multiple of 16
+    assert lib.idx_diag_hbm_read(FAKE, 0, 4, out, None) == bd.IDX_EINVAL
+    assert lib.idx_diag_hbm_read(FAKE, 1024, 0, out, None) == bd.IDX_EINVAL
+    assert lib.idx_diag_hbm_read(FAKE + 8, 1024, 4, out, None) == bd.IDX_EALIGN
+    assert lib.idx_diag_hbm_read(FAKE, 1024, 4, None, None) == bd.IDX_EINVAL
+
+
 def test_diag_mfma_checks(lib):
     out = ctypes.c_void_p(FAKE)
     assert lib.idx_diag_mfma(2, 1, 1, out, None) == bd.IDX_EINVAL

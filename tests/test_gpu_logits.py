@@ -115,7 +115,10 @@ def edge_workload(H, n_q, P, ctx, fmt=wl.MXFP4):
     (20, 2, 32, [0, 5, 100], wl.MXFP4),        # ragged head tile, empty sequence, n_q > ctx
     (48, 1, 256, [700, 513], wl.MXFP4),        # 3 head tiles, large pages
     (128, 1, 64, [129, 64], wl.MXFP4),         # the largest head count
-    (16, 9, 64, [200, 9, 3], wl.MXFP4),        # 9 head tiles -> the prefill kernel with several sequences
+    (16, 9, 64, [200, 9, 3], wl.MXFP4),        # nine rows of one head tile: the row-split decode kernel
+    (48, 5, 64, [300, 70, 5], wl.MXFP4),       # row-split decode kernel, three head tiles per row
+    (48, 5, 64, [300, 70, 5], wl.FP8),         # the same in FP8
+    (32, 8, 128, [900, 260], wl.FP8),          # row-split decode kernel, two head tiles, FP8, 16 tiles in all
     (32, 33, 128, [40, 1000], wl.MXFP4),       # prefill kernel, causal rows crossing chunk edges
     (32, 33, 128, [40, 1000], wl.FP8),         # the same in FP8
     (20, 17, 64, [17, 700, 0], wl.FP8),        # FP8 prefill, ragged head tile, an empty sequence
@@ -159,17 +162,33 @@ def test_scorer_deterministic():
 
 
 @pytest.mark.parametrize("scale", [
-    {"B": 12, "n_q": 2, "H": 48},            # two rows per wave group: two chunk lanes per block
-    {"B": 8, "n_q": 4, "H": 32},             # four rows: one chunk lane, every wave a row
+    {"B": 12, "n_q": 2, "H": 48},            # two rows: two waves score, all four fetch K
+    {"B": 8, "n_q": 4, "H": 32},             # four rows: every wave scores
     {"B": 9, "n_q": 3, "H": 64, "ctx": 300}, # short contexts: one or two chunks per row
 ])
 @pytest.mark.parametrize("fmt", [wl.MXFP4, wl.FP8])
 def test_logits_streaming_shapes(scale, fmt):
-    """The streaming row-split scorer (2-4 query rows with more than four head tiles in all)
-    on mixed context lengths, page 64, an offset pool with gaps: every row against the
-    oracle, masked cells untouched."""
+    """The streaming scorer for 2-4 query rows with more than four head tiles in all (K
+    shared through LDS by the block's row waves, balanced runs of chunks) on mixed context
+    lengths, page 64, an offset pool with gaps: every row against the oracle, masked cells
+    untouched."""
     W = wl.make_workload(3, kv_format=fmt, scale=scale)
     G.say(f"logits streaming form fmt={fmt} {scale}")
     d = setup_scorer(W, fmt)
     logits = run_scorer(W, d)
     check(W, d, logits, np.arange(W.rows), f"stream {scale}/fmt{fmt}")
+
+
+@pytest.mark.parametrize("n_q,fmt", [(3, wl.MXFP4), (2, wl.FP8)])
+def test_logits_streaming_many_sequences(n_q, fmt):
+    """150 sequences of mixed lengths (three per lane in the device-side prefix that sizes
+    the balanced runs), some empty or shorter than n_q: every row against the oracle."""
+    rng = np.random.default_rng(90 + n_q)
+    ctx = rng.integers(0, 1500, 150)
+    ctx[::17] = 0
+    ctx[5::23] = 1
+    W = edge_workload(64, n_q, 64, ctx.tolist(), fmt)
+    G.say(f"logits streaming form, 150 sequences n_q={n_q} fmt={fmt}")
+    d = setup_scorer(W, fmt)
+    logits = run_scorer(W, d, stride=W.max_ctx + 3)
+    check(W, d, logits, np.arange(W.rows), f"stream 150 seqs nq{n_q}/fmt{fmt}")

@@ -150,7 +150,7 @@ def test_step_large_pool(fmt):
     (1, wl.MXFP4, {"B": 16, "H": 64}),            # 64 heads of one query token: four head tiles
     (1, wl.FP8, {"B": 6, "H": 64}),
     (3, wl.MXFP4, {"B": 8, "H": 16}),             # three query tokens of 16 heads, page 64, offset pool
-    (3, wl.MXFP4, {"B": 10}),                     # three query tokens of 64 heads: the row-split scorer
+    (3, wl.MXFP4, {"B": 10}),                     # three query tokens of 64 heads: the streaming scorer
     (1, wl.MXFP4, {"B": 12, "H": 32, "n_q": 2}),  # two query tokens of 32 heads
 ])
 def test_step_more_head_tiles(cfg, fmt, scale):
