@@ -159,3 +159,30 @@ def test_bytes_per_token_are_the_pages_numbers():
     assert oracle.bytes_per_token(oracle.FMT_FP8) == ind.GOLDEN["fp8_bytes_per_token"]["value"]
     # 68 = 128 nibbles (64 B) + one E8M0 byte per 32-element block
     assert 128 // 2 + 128 // ind.GOLDEN["mx_block_size"]["value"] == 68
+
+
+def test_fp8_q_quant_codes_against_exact_rationals():
+    """oracle.q_quant_fp8: every code is the exact-rational OCP e4m3 code (nearest, ties to
+    even, saturating) of q / sq for the head's scale sq, the head's largest element lands on
+    one of the top codes, and the weight fold is the plain product.  The scale rule itself
+    (sq = fp32(amax / 448)) is the stated reading of the FP8 arm and stays parity unpinned."""
+    import numpy as np
+    from sparse_attention_indexer_idx_amd import workloads as wl
+    rng = np.random.default_rng(31)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((5, 3, 128), dtype=np.float32) * 3.0)
+    q[0, 0] = 0                                   # an all-zero head: scale 0, sign-only codes
+    w = rng.standard_normal((5, 3)).astype(np.float32)
+    codes, wo = oracle.q_quant_fp8(q, w)
+    for t in range(5):
+        for h in range(3):
+            x = [ind.bf16_fraction(int(b)) for b in q[t, h]]
+            amax = max(abs(v) for v in x)
+            sq = np.float32(float(amax) / 448.0)
+            assert wo[t, h] == np.float32(np.float64(w[t, h]) * np.float64(sq))
+            if amax == 0:
+                assert np.all((codes[t, h] & 0x7F) == 0) and wo[t, h] == 0
+                continue
+            for i in range(128):
+                want = ind.e4m3_code_exact(x[i] / Fraction(float(sq)), x[i] < 0)
+                assert codes[t, h, i] == want, (t, h, i)
+            assert max(int(c) & 0x7F for c in codes[t, h]) >= 0x7D
