@@ -6,10 +6,13 @@
 namespace idx {
 namespace {
 
+// Rows are taken last first: the query rows of a sequence are its newest tokens, so later
+// rows are at least as long (causal prefill: row j has j + 1 cells), and the longest rows
+// then start first instead of forming a tail.
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   __shared__ TopkShared<NT, EPT> sh;
-  const int64_t r = blockIdx.x;
+  const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int b = (int)(r / a.n_q), j = (int)(r % a.n_q);
   const int n_b = min(max(a.ctx[b], 0), a.max_ctx);
   int n = n_b - a.n_q + 1 + j;
