@@ -134,6 +134,13 @@ def fused_source_hash():
     return source_hash([os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in FUSED_SOURCES])
 
 
+TOPK_SOURCES = ("topk.hip", "topk_row.hpp", "device_common.hpp", "launch.hpp")
+
+
+def topk_source_hash():
+    return source_hash([os.path.join(ROOT, "sparse_attention_indexer_idx_amd", "csrc", f) for f in TOPK_SOURCES])
+
+
 def _short_kernel(name):
     import re
     m = re.search(r"((?:\w+::)*\w+(?:<[^()]*>)?)\(", name.replace("(anonymous namespace)::", ""))
@@ -200,8 +207,10 @@ def summarize(dirs, traffic_key=None, calib_mib=0):
     p = os.path.join(ROOT, "profiles", "traffic.json")
     d = json.load(open(p)) if os.path.exists(p) else {}
     fused = lambda k: k.startswith("decode_step_kernel")
+    topk = lambda k: k.startswith("topk_kernel")
     for key, pred, shash in ((traffic_key, scorer, scorer_source_hash()),
-                             (traffic_key + "_fused", fused, fused_source_hash())):
+                             (traffic_key + "_fused", fused, fused_source_hash()),
+                             (traffic_key + "_topk", topk, topk_source_hash())):
         if not any(pred(k) and c == "FETCH_SIZE" for (k, g, c) in counters):
             continue
         _, fetch, _ = pick(pred, "FETCH_SIZE", big)
@@ -480,6 +489,16 @@ def scorer_roof(R, ab, s_mean):
     return roof
 
 
+def topk_roof(R, ab, t_mean):
+    """Roofline of the top-k: logits read (valid cells) and indices written over its mean
+    duration, against HBM."""
+    gbs = ab["topk"] / (t_mean * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["topk"], "kernel": "topk_kernel",
+            "traffic": traffic_from_profiles(f"cfg{R.config}_{R.kv}_topk", topk_source_hash()),
+            "source_hash": topk_source_hash()}
+
+
 def summary(R, held, steps, cpu_budget_s, with_cpu):
     """One workload measured the short way: each kernel alone back to back, the step
     replayed from HIP graphs, the scorer's and the top-k's rooflines, and the oracle on a
@@ -499,16 +518,13 @@ def summary(R, held, steps, cpu_budget_s, with_cpu):
     L = R.replicas * max(1, -(-8 // R.replicas))
     graph_ms, _ = time_graph(R.torch, R.fused_step if fused else R.step, L, steps)
     ab = algorithmic_bytes(W, R.fmt, len(R.new))
-    tk_gbs = ab["topk"] / (t_mean * 1e-6) / 1e9
     d = {"workload": W.name, "kv": R.kv, "B": W.B, "n_q": W.n_q, "H": W.H, "page_size": W.page_size,
          "max_ctx": W.max_ctx, "topk": W.topk, "cache": R.cache,
          "step_us": round(graph_ms * 1e3, 3),
          "path": "fused idx_decode_step" if fused else "idx_k_store + idx_logits_paged + idx_topk",
          "k_store_us": round(k_mean, 3), "score_us": round(s_mean, 3), "topk_us": round(t_mean, 3),
          "scorer_roofline": scorer_roof(R, ab, s_mean),
-         "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(tk_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["topk"],
-                           "kernel": "topk_kernel"}}
+         "topk_roofline": topk_roof(R, ab, t_mean)}
     if with_cpu:
         d["cpu_baseline"] = cpu_baseline(W, R.fmt, cpu_budget_s, max_rows=32)
     return d
@@ -614,7 +630,6 @@ def main():
                       "note": "the whole step in one launch (K store + scorer + top-k), the top-k tail's "
                               "latency included"}
     step_us = ms_per_step * 1e3
-    tk_gbs = ab["topk"] / (t_mean * 1e-6) / 1e9
     result = {
         "metric": "indexer score+top-k us/call; HBM TB/s (decode), FP4 TFLOPS (prefill)",
         "value": round(step_us, 3),
@@ -644,9 +659,7 @@ def main():
         # scorer (the dominant one of the three); the scorer alone is always listed too
         "roofline": roof if fused_us is None else fused_roof,
         "scorer_roofline": roof,
-        "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(tk_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["topk"],
-                          "kernel": "topk_kernel"},
+        "topk_roofline": topk_roof(R, ab, t_mean),
         "q_prep_us": None if qprep_us is None else round(qprep_us, 3),
         "candidates_us": cand_us,
         "scorer_tflops": round(ab["flops"] / (s_mean * 1e-6) / 1e12, 2),

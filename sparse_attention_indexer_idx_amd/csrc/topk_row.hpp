@@ -322,6 +322,8 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   // Keys: only the group of rounds that holds the row's end needs the per-cell length mask;
   // groups wholly inside the row take the unmasked key (a uniform branch per group keeps
   // the masks from being computed ahead for every round and held in registers).
+  // Groups wholly past the row are not computed: no phase reads their keys (for_rounds
+  // skips them, and the exact path re-reads the row).
   uint32_t key[EPT];
   constexpr int kGroup = EPT < 8 ? EPT : 8;
 #pragma unroll
@@ -329,9 +331,12 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
     if ((g + kGroup) * NT <= n) {
 #pragma unroll
       for (int e = g; e < g + kGroup; ++e) key[e] = map.key_full(raw[e]);
-    } else {
+    } else if (g == 0 || g * NT < n) {
 #pragma unroll
       for (int e = g; e < g + kGroup; ++e) key[e] = map.key(raw[e], e * NT + tid - n);
+    } else {
+#pragma unroll
+      for (int e = g; e < g + kGroup; ++e) key[e] = 0u;
     }
   }
   if constexpr (Map::kCountValid) {
