@@ -69,28 +69,33 @@ __device__ __forceinline__ void worker_run(const LogitsArgs& a, int worker, int 
   c1 = __builtin_amdgcn_readlane(cc1, L);
 }
 
+// Page ids of a worker's run, lane l holding the table entry `first + l` (clamped to the
+// row), loaded once beside the query tiles: a chunk's K address then needs no page-table
+// round trip inside the loop.  The launch sizes the runs so that every run's pages fit
+// this 64-entry window; pages past it (only the loads issued beyond a run's end ask for
+// them, and those never use the id) read as an invalid id.
+struct RunPages {
+  int first, last;
+  int32_t ids;
+  __device__ __forceinline__ RunPages(const int32_t* row, int first_pg, int last_pg, int lane)
+      : first(first_pg), last(last_pg), ids(row[std::min(first_pg + lane, last_pg)]) {}
+  __device__ __forceinline__ int32_t at(int pg) const {  // pg uniform and >= first
+    const int rel = std::min(pg, last) - first;
+    return rel < 64 ? __builtin_amdgcn_readlane(ids, rel) : -1;
+  }
+};
+
 template <int FMT, int HT, bool NT_LOADS, int M>
 __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  int worker, n_workers, j;
-  if (a.n_q == 1) {
-    worker = blockIdx.x * 4 + wave;
-    n_workers = gridDim.x * 4;
-    j = 0;
-  } else {
-    if (wave >= a.n_q) return;
-    worker = blockIdx.x;
-    n_workers = gridDim.x;
-    j = wave;
-  }
   int b, c, c_end;
-  worker_run<M>(a, worker, n_workers, lane, b, c, c_end);
+  worker_run<M>(a, blockIdx.x * 4 + wave, gridDim.x * 4, lane, b, c, c_end);
   if (b < 0 || c >= c_end) return;  // uniform: no run for this worker
-  const int64_t r = (int64_t)b * a.n_q + j;
+  const int64_t r = b;  // one query row per sequence
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int last_page = (a.max_ctx - 1) >> lgP;
-  const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
+  const RunPages pages(a.page_table + (int64_t)b * a.max_pages, (64 * c) >> lgP, last_page, lane);
 
   v8i qa[HT];
   uint32_t qs[HT];
@@ -101,8 +106,7 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
     qw[ht] = load_w_tile(a, r, ht, lane);
   }
   const int n_b = uniform(std::min(std::max(a.ctx[b], 0), a.max_ctx));
-  const int n_r = valid_len(n_b, a.n_q, j);
-  const int n_ch = std::min((n_r + 63) >> 6, c_end);  // this row's chunks inside the run
+  const int n_ch = std::min((n_b + 63) >> 6, c_end);  // the row's chunks inside the run
 
   const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);  // page ids are int32
   // Issue the four K tiles of chunk cc (any cc: past the row they read page 0 row 0).
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int s0 = 64 * cc + 16 * t;
-      const int32_t pid = uniform(ptb[std::min(s0 >> lgP, last_page)]);
+      const int32_t pid = pages.at(s0 >> lgP);
       const bool valid_page = pid >= 0 && pid < np32;
       const bool use = live && valid_page;
       const uint8_t* page = a.pool.base + (use ? (int64_t)pid : 0) * a.pool.stride;
@@ -145,10 +149,9 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
     }
     const float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
     const int s = 64 * cc + lane;
-    if (s < n_r) out_row[s] = logit;
+    if (s < n_b) out_row[s] = logit;
   };
 
-  if (c >= n_ch) return;  // uniform: this row ends before the run (rows j < n_q - 1)
   KTile<FMT> A[4], B[4];
   bool okA[4], okB[4];
   issue(c, A, okA);
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
 // a chunk's four K tiles into registers and then LDS, and wave j < n_q scores query row j
 // from all four tiles in LDS, so a chunk's K leaves HBM once per block.  Lane l of every
 // wave reads back the operand lane l fetched, which is its own MFMA operand for that tile.
-// Two LDS buffers alternate with one barrier per chunk; the next chunk's fetch is in
-// flight while the current one is scored.  The chunk loop runs over the longest row of
+// Two LDS buffers alternate with one barrier per chunk; the fetches of the next two
+// chunks are in flight while the current one is scored.  The chunk loop runs over the longest row of
 // the sequence (row n_q - 1), the same for every wave; each row stores only its own cells.
 template <int FMT>
 struct alignas(16) StreamStage {
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
   const int64_t r = (int64_t)b * a.n_q + j;
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
   const int last_page = (a.max_ctx - 1) >> lgP;
-  const int32_t* __restrict__ ptb = a.page_table + (int64_t)b * a.max_pages;
+  const RunPages pages(a.page_table + (int64_t)b * a.max_pages, (64 * c0) >> lgP, last_page, lane);
   const int32_t np32 = (int32_t)std::min<int64_t>(a.pool.num_pages, INT32_MAX);  // page ids are int32
 
   v8i qa[HT];
@@ -207,24 +210,32 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
   const int n_end = std::min((n_b + 63) >> 6, c_end);  // the longest row's chunks in the run
 
   auto page_of = [&](int cc, int t, bool& ok) {  // uniform
-    const int s0 = 64 * cc + 16 * t;
-    const int32_t pid = uniform(ptb[std::min(s0 >> lgP, last_page)]);
+    const int32_t pid = pages.at((64 * cc + 16 * t) >> lgP);
     ok = pid >= 0 && pid < np32;
     return pid;
   };
-  // this wave's tile (t = wave) of chunk cc; past the run it reads page 0 row 0
+  // this wave's tile (t = wave) of chunk cc; past the run it reads page 0 row 0.  MXFP4
+  // loads the token's four E8M0 bytes as one word, shifted to the lane's byte when staged
+  // (a byte load here made the compiler wait for every load in flight at the loop head).
   auto fetch = [&](int cc) {
     bool okk;
     const int32_t pid = page_of(cc, wave, okk);
     const bool use = okk && cc < n_end;
     const uint8_t* page = a.pool.base + (use ? (int64_t)pid : 0) * a.pool.stride;
-    return load_k_tile<FMT, false>(page, P, use ? ((64 * cc + 16 * wave) & (P - 1)) : 0, lane);
+    const int row0 = use ? ((64 * cc + 16 * wave) & (P - 1)) : 0;
+    if (FMT == 1) return load_k_tile<FMT, false>(page, P, row0, lane);
+    KTile<FMT> k;
+    const uint32_t tok = (uint32_t)(row0 + (lane & 15));
+    const u32x4 x = *(const u32x4*)(page + (tok * 64u + 16u * (uint32_t)(lane >> 4)));
+    k.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+    k.scale = *(const uint32_t*)(page + ((uint32_t)P * 64u + tok * 4u));
+    return k;
   };
   auto stash = [&](int buf, const KTile<FMT>& k) {
     st.data[buf][wave][lane][0] = make_uint4((uint32_t)k.v[0], (uint32_t)k.v[1], (uint32_t)k.v[2], (uint32_t)k.v[3]);
     if (FMT == 1)
       st.data[buf][wave][lane][FMT] = make_uint4((uint32_t)k.v[4], (uint32_t)k.v[5], (uint32_t)k.v[6], (uint32_t)k.v[7]);
-    st.scale[buf][wave][lane] = k.scale;
+    st.scale[buf][wave][lane] = FMT == 0 ? k.scale >> (8 * (lane >> 4)) : k.scale;
   };
   auto unstash = [&](int buf, int t) {
     KTile<FMT> k;
@@ -241,13 +252,15 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
   const float qnan = __builtin_nanf("");
   float* __restrict__ out_row = a.logits + r * a.lstride;
 
-  KTile<FMT> nxt = fetch(c0);
-  for (int cc = c0; cc < n_end; ++cc) {  // block-uniform trip count
+  // Chunk cc: stage its tile (fetched two chunks earlier into register slot R, the LDS
+  // buffer of the same parity), refill R with chunk cc + 2, and score it from LDS.  The
+  // two slots alternate, so no register copy waits on a load in flight.
+  auto step = [&](int cc, KTile<FMT>& R) {
     const int buf = (cc - c0) & 1;
-    stash(buf, nxt);
-    nxt = fetch(cc + 1);
+    stash(buf, R);
+    R = fetch(cc + 2);
     __syncthreads();
-    if (scorer && 64 * cc < n_r) {  // uniform per wave
+    if (scorer && cc < n_end && 64 * cc < n_r) {  // uniform per wave
       float p[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -264,6 +277,14 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
       const int s = 64 * cc + lane;
       if (s < n_r) out_row[s] = logit;
     }
+  };
+  // Chunks go in pairs with one exit test per pair (an odd run stages one chunk past its
+  // end and scores nothing from it): an exit between the two steps gave the compiler a path
+  // on which it waited for every load in flight at the loop head.
+  KTile<FMT> A = fetch(c0), B = fetch(c0 + 1);
+  for (int cc = c0; cc < n_end; cc += 2) {  // block-uniform trip count
+    step(cc, A);
+    step(cc + 1, B);
   }
 }
 
@@ -305,12 +326,17 @@ hipError_t launch_logits_stream(const LogitsArgs& a, int num_cus, hipStream_t s)
   if (a.max_ctx == 0) return hipSuccess;
   if (!logits_stream_takes(a.B, a.n_q, a.max_ctx)) return hipErrorInvalidValue;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
-  // About eight waves per SIMD over the device, at least two workers per sequence (so the
-  // balanced runs have room), and no more workers than chunks.
+  // Two waves per SIMD of one-row workers, or six blocks per CU of several-row workers
+  // (fewer, longer runs measured faster than a fuller device: the page ids and query
+  // tiles are loaded once per run); at least two workers per sequence (so the balanced
+  // runs have room), and no more workers than chunks.  Runs are at most q_cap chunks, so
+  // that a run's pages fit the 64-entry page-id window: with spare >= max_units / q_cap
+  // workers past one per sequence, the device's q = ceil(U / spare) <= q_cap.
   const int64_t max_units = (int64_t)a.B * ((a.max_ctx + 63) / 64);
-  const int64_t want_waves = (int64_t)num_cus * 32;
-  int64_t workers = a.n_q == 1 ? want_waves : want_waves / 4;
+  const int64_t q_cap = std::max<int64_t>(1, (int64_t)63 * a.pool.page_size / 64);
+  int64_t workers = a.n_q == 1 ? (int64_t)num_cus * 8 : (int64_t)num_cus * 6;
   workers = std::max<int64_t>(workers, 2 * (int64_t)a.B);
+  workers = std::max<int64_t>(workers, (max_units + q_cap - 1) / q_cap + a.B);
   workers = std::min<int64_t>(workers, max_units + a.B);
   const int64_t blocks = a.n_q == 1 ? (workers + 3) / 4 : workers;
   return a.pool.kv_format == 0 ? launch_stream_fmt<0>(a, dim3((unsigned)blocks), ht, s)

@@ -179,6 +179,17 @@ def test_logits_streaming_shapes(scale, fmt):
     check(W, d, logits, np.arange(W.rows), f"stream {scale}/fmt{fmt}")
 
 
+def test_logits_streaming_long_runs_small_pages():
+    """One-row streaming form with 16-token pages and runs of about a dozen 64-token chunks
+    (about 50 pages per run, read from the run's page-id window): every row against the
+    oracle.  1.55M tokens over four sequences, so that the streaming form takes the call."""
+    W = edge_workload(4, 1, 16, [600_000, 550_000, 300_000, 100_000])
+    G.say("logits streaming form, long runs over 16-token pages")
+    d = setup_scorer(W, wl.MXFP4)
+    logits = run_scorer(W, d)
+    check(W, d, logits, np.arange(W.rows), "stream long runs P16")
+
+
 @pytest.mark.parametrize("n_q,fmt", [(3, wl.MXFP4), (2, wl.FP8)])
 def test_logits_streaming_many_sequences(n_q, fmt):
     """150 sequences of mixed lengths (three per lane in the device-side prefix that sizes
