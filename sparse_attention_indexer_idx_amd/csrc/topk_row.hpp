@@ -357,9 +357,19 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   __syncthreads();
 
   // ---- pass 1: the top D1 bits of every valid cell ----
-  for_rounds<EPT>(ne, [&](int e) {
-    if (key[e] != 0u) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
-  });
+  // A group of rounds wholly inside a dense row holds only valid keys and adds every one
+  // (no per-cell branch); other groups skip key 0.
+#pragma unroll
+  for (int g = 0; g < EPT; g += kGroup) {
+    if (!Map::kCountValid && (g + kGroup) * NT <= n) {
+#pragma unroll
+      for (int e = g; e < g + kGroup; ++e) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
+    } else if (g == 0 || g * NT < n) {
+#pragma unroll
+      for (int e = g; e < g + kGroup; ++e)
+        if (key[e] != 0u) atomicAdd(&sh.hist[key[e] >> C::Shift], 1u);
+    }
+  }
   __syncthreads();
   select_digit<NT, C::Bins>(sh, k);
   const uint32_t d1 = (uint32_t)sh.sel_digit;
