@@ -94,10 +94,12 @@ template <int FMT>
 struct alignas(16) PrefillStage {
   uint4 data[2][kStageTiles][64][FMT == 0 ? 1 : 2];
   uint32_t scale[2][kStageTiles][64];
+  float out[4][kPrefillRowsPerWave][32];  // per wave: two tiles' logits, re-read as pairs
 };
 
 template <int FMT, int HT>
-__global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, PrefillPlan plan) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT != 0 ? 1 : HT == 1 ? 6 : HT == 2 ? 4 : 1))) void logits_prefill_kernel(
+    LogitsArgs a, PrefillPlan plan) {
   __shared__ PrefillStage<FMT> st;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -142,9 +144,15 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
       qw[g][ht] = load_w_tile(a, r, ht, lane);
     }
   }
-  const int jr = j0 + (lane >> 4);
-  const int my_n = jr < a.n_q ? valid_len(n_b, a.n_q, jr) : 0;
-  float* out_row = a.logits + ((int64_t)b * a.n_q + std::min(jr, a.n_q - 1)) * a.lstride;
+  // stores of a tile pair: lane l writes row j0 + 2i + l/32, token l%32
+  float* pair_row[2];
+  int pair_n[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int jr = j0 + 2 * i + (lane >> 5);
+    pair_n[i] = jr < a.n_q ? std::min(valid_len(n_b, a.n_q, jr), t_end) : 0;  // t_end: this unit's chunk
+    pair_row[i] = a.logits + ((int64_t)b * a.n_q + std::min(jr, a.n_q - 1)) * a.lstride;
+  }
   const float qnan = __builtin_nanf("");
 
   constexpr int TPW = kStageTiles / 4;  // tiles each wave fetches per group
@@ -187,25 +195,39 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(LogitsArgs a, Prefi
 #pragma unroll
     for (int i = 0; i < TPW; ++i) nxt[i] = fetch(gg + 1, i);  // past the end: page 0 row 0, never stashed
     __syncthreads();
+    // Tiles go in pairs: both tiles' logits (lane l: row l/16, token l%16 of each) pass
+    // through the wave's LDS rows and come back as 32 consecutive tokens of two rows per
+    // store, so each store writes two rows' 128-byte runs instead of four half runs.
 #pragma unroll
-    for (int t = 0; t < kStageTiles; ++t) {
+    for (int t = 0; t < kStageTiles; t += 2) {
       const int s0 = t_begin + 16 * kStageTiles * gg + 16 * t;
       if (s0 < t_end) {  // uniform
-        const KTile<FMT> kt = unstash(buf, t);
-        float p[kPrefillRowsPerWave];
+        float* orow = st.out[wave][lane >> 4];
 #pragma unroll
-        for (int g = 0; g < kPrefillRowsPerWave; ++g) {
-          float acc = 0.0f;
+        for (int h = 0; h < 2; ++h) {
+          const KTile<FMT> kt = unstash(buf, t + h);
+          float p[kPrefillRowsPerWave];
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht)
-            acc = relu_dot_acc(mfma<FMT>(qa[g][ht], qs[g][ht], kt), qw[g][ht], acc, ht == 0);
-          p[g] = acc;
+          for (int g = 0; g < kPrefillRowsPerWave; ++g) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+              acc = relu_dot_acc(mfma<FMT>(qa[g][ht], qs[g][ht], kt), qw[g][ht], acc, ht == 0);
+            p[g] = acc;
+          }
+          float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
+          if (FMT == 1) logit *= __uint_as_float(kt.scale);
+          if (!tile_ok(s0 + 16 * h)) logit = qnan;
+          orow[16 * h + (lane & 15)] = logit;
         }
-        float logit = reduce4_transpose(p[0], p[1], p[2], p[3]);
-        if (FMT == 1) logit *= __uint_as_float(kt.scale);
-        if (!tile_ok(s0)) logit = qnan;
-        const int s = s0 + (lane & 15);
-        if (s < my_n) out_row[s] = logit;
+        __builtin_amdgcn_wave_barrier();  // the reads below take other lanes' writes
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int s = s0 + (lane & 31);
+          const float v = st.out[wave][2 * i + (lane >> 5)][lane & 31];
+          if (s < pair_n[i]) pair_row[i][s] = v;
+        }
+        __builtin_amdgcn_wave_barrier();  // and the next pair's writes come after them
       }
     }
   }
