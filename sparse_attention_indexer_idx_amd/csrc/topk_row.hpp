@@ -62,7 +62,7 @@ struct Cfg {
 
 template <int NT, int EPT>
 struct alignas(16) TopkShared {
-  uint32_t hist[Cfg<NT>::Bins];
+  uint32_t hist[Cfg<NT>::Bins + 256];  // pass 1's digits, then a large bucket's second digits
   uint64_t cand[kRankCap];  // (key << 32) | ~index: one unsigned compare orders the bucket
   int32_t wave_tot[2 * (NT / 64)];
   int32_t cnt_gt[EPT * (NT / 64)];
@@ -204,6 +204,51 @@ struct CandidateRow {
   }
 };
 
+// Ranking a large bucket (nc^2 > kRank2Factor * NT) by a second digit: the 8 key bits below
+// pass 1's digit.  The bucket is counting-sorted by that digit into LDS (digits descending;
+// the order inside a digit's run is whatever the atomics give), and each candidate's rank is
+// the number of candidates in higher digits plus those of its own run ordered before it by
+// (key desc, index asc) — the same exact rank, and so the same output slot, as the direct
+// ranking, at a cost of the run length instead of the bucket size per candidate.  The 256
+// counters follow pass 1's bins (cleared with them); the run ends and the sorted list reuse
+// pass 1's words, dead by then.  Three barriers.  Out of line: inlined, it pushed the
+// 256-thread form past its 96-register budget (four registers spilled on the common path).
+constexpr int kRank2Factor = 32;
+
+template <int NT, class SH, class Map>
+__device__ __attribute__((noinline)) void rank_by_second_digit(SH& sh, int nc, int kk, int tot_gt,
+                                                               int32_t* __restrict__ out, const Map map) {
+  using C = Cfg<NT>;
+  static_assert(C::Bins >= 256 + 2 * kRankCap, "second-level ranking needs pass 1's histogram words");
+  constexpr int S2 = C::Shift - 8;
+  const int tid = threadIdx.x;
+  uint32_t* cnt = sh.hist + C::Bins;  // per second digit: candidates
+  uint32_t* end = sh.hist;            // per second digit: end of its run (a cursor while sorting)
+  uint64_t* sorted = reinterpret_cast<uint64_t*>(sh.hist + 256);
+  auto digit2 = [](uint64_t c) { return (uint32_t)(c >> (32 + S2)) & 255u; };
+  for (int i = tid; i < nc; i += NT) atomicAdd(&cnt[digit2(sh.cand[i])], 1u);
+  __syncthreads();
+  // start of each digit's run: the candidates of higher digits (thread t holds digit 255 - t)
+  const int v = tid < 256 ? (int)cnt[255 - tid] : 0;
+  int total;
+  const int before = block_excl_scan<NT>(v, sh.wave_tot, total);
+  if (tid < 256) end[255 - tid] = (uint32_t)before;
+  __syncthreads();
+  for (int i = tid; i < nc; i += NT) {
+    const uint64_t c = sh.cand[i];
+    sorted[atomicAdd(&end[digit2(c)], 1u)] = c;
+  }
+  __syncthreads();
+  for (int j = tid; j < nc; j += NT) {
+    const uint64_t me = sorted[j];
+    const uint32_t d = digit2(me);
+    const int hi = (int)end[d], lo = hi - (int)cnt[d];
+    int rank = lo;
+    for (int i = lo; i < hi; ++i) rank += sorted[i] > me ? 1 : 0;
+    if (rank < kk) out[tot_gt + rank] = map.token((int)~(uint32_t)me);
+  }
+}
+
 // The exact path for a row whose boundary bucket holds more keys than the ranking list
 // (long runs of equal values).  It re-reads the row's cells (from cache) in rolled loops
 // instead of taking the caller's register keys, so it holds no per-round state and the
@@ -318,7 +363,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     raw[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, e * NT * 4, 0));
-  for (int i = tid; i < C::Bins / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < C::Bins / 4 + 64; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
   // Keys: only the group of rounds that holds the row's end needs the per-cell length mask;
   // groups wholly inside the row take the unmasked key (a uniform branch per group keeps
   // the masks from being computed ahead for every round and held in registers).
@@ -397,9 +442,14 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
       if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
     });
     // Rank of each candidate among the bucket by (key desc, index asc); composites are
-    // distinct, so the ranks are a permutation of 0..nc-1.  G adjacent lanes share one
-    // candidate (G = NT / nc rounded to a power of two, at most 64), each counting a
-    // strided part of the list, and a lane-xor reduction sums their counts.
+    // distinct, so the ranks are a permutation of 0..nc-1.
+    if (nc * nc > kRank2Factor * NT) {  // uniform: a large bucket
+      rank_by_second_digit<NT>(sh, nc, kk, tot_gt, out, map);
+      return;
+    }
+    // G adjacent lanes share one candidate (G = NT / nc rounded to a power of two, at
+    // most 64), each counting a strided part of the list, and a lane-xor reduction sums
+    // their counts.
     int np2 = 1;
     while (np2 < nc) np2 <<= 1;
     const int G = max(1, min(64, NT / np2));

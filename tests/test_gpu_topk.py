@@ -147,6 +147,28 @@ def test_topk_bucket_sizes_exact(rows, n, k, lo, hi, step):
         assert np.array_equal(np.sort(got[r]), np.sort(ref[r])), f"row {r}"
 
 
+@pytest.mark.parametrize("rows,n,n_hi,n_bucket,k,width", [
+    (1100, 4096, 1000, 300, 1100, 2.0 ** -11),   # 256 threads (20 key bits in the two digits)
+    (8, 8192, 900, 700, 1200, 2.0 ** -12),       # 1024 threads (21 key bits in the two digits)
+])
+def test_topk_bucket_one_second_digit_exact(rows, n, n_hi, n_bucket, k, width):
+    """A large boundary bucket whose keys also share the second-level digit (values in
+    [1, 1 + width): the same first and second digit, distinct low bits), so the whole bucket
+    is one run of the second-level ranking; cells above it in [4, 8), below it in [-8, -4)."""
+    rng = np.random.default_rng(rows + n + k)
+    lg = rng.uniform(-8.0, -4.0, size=(rows, n)).astype(np.float32)
+    for r in range(rows):
+        cells = rng.permutation(n)
+        lg[r, cells[:n_hi]] = rng.uniform(4.0, 8.0, n_hi)
+        lg[r, cells[n_hi:n_hi + n_bucket]] = 1.0 + rng.uniform(0.0, width, n_bucket)
+    ctx = np.full(rows, n, np.int32)
+    G.say(f"topk one second digit rows={rows} n={n} bucket={n_bucket} k={k}")
+    got = gpu_topk(G.dev(lg), ctx, rows, 1, k)
+    ref = oracle.topk(lg, ctx, 1, k)
+    for r in range(rows):
+        assert np.array_equal(np.sort(got[r]), np.sort(ref[r])), f"row {r}"
+
+
 def test_graph_replay_matches_eager():
     """K store + scorer + top-k captured in a HIP graph: every replay (with eager work and
     synchronisation between replays) reproduces the eager results byte for byte."""
