@@ -10,13 +10,14 @@
 //   one block scan of two per-thread counts (cells above the bucket, cells in it) gives
 //   every thread the output slots of its selected cells and the list slots of its
 //   bucket cells;
-//   the bucket (usually a few dozen keys) is resolved by ranking: each candidate counts
-//   the candidates ordered before it by (key desc, index asc); rank < the number still
-//   needed is selected, and the rank is its output slot.
+//   the bucket (tens to a few hundred keys) is resolved by ranking: it is counting-sorted
+//   by the next 8 key bits, and each candidate counts the candidates ordered before it by
+//   (key desc, index asc) in higher digits and in its own digit's run; rank < the number
+//   still needed is selected, and the rank is its output slot.
 // A row whose bucket is larger than the ranking list (long runs of equal values) takes a
-// slower exact path: two more histogram passes over the register keys fix K*, and ranks
-// in index order come from wave ballots and per-(round, wave) counts.  Either way equal
-// logits resolve toward the smaller index and the output order is deterministic.
+// slower exact path: two more histogram passes over the keys fix K*, and ranks in index
+// order come from wave ballots and per-(round, wave) counts.  Either way equal logits
+// resolve toward the smaller index and the output order is deterministic.
 #pragma once
 
 #include "device_common.hpp"
@@ -204,20 +205,19 @@ struct CandidateRow {
   }
 };
 
-// Ranking a large bucket (nc^2 > kRank2Factor * NT) by a second digit: the 8 key bits below
-// pass 1's digit.  The bucket is counting-sorted by that digit into LDS (digits descending;
-// the order inside a digit's run is whatever the atomics give), and each candidate's rank is
-// the number of candidates in higher digits plus those of its own run ordered before it by
-// (key desc, index asc) — the same exact rank, and so the same output slot, as the direct
-// ranking, at a cost of the run length instead of the bucket size per candidate.  The 256
+// Ranking the bucket by a second digit, the 8 key bits below pass 1's digit.  The bucket is
+// counting-sorted by that digit into LDS (digits descending; the order inside a digit's run
+// is whatever the atomics give), and each candidate's rank is the number of candidates in
+// higher digits plus those of its own run ordered before it by (key desc, index asc): the
+// exact rank, and so the output slot, at a cost of the run length per candidate instead of
+// the bucket size.  (Measured against ranking over the whole bucket with lane groups sharing
+// a candidate: as fast or faster at every bucket size of the benchmark rows.)  The 256
 // counters follow pass 1's bins (cleared with them); the run ends and the sorted list reuse
 // pass 1's words, dead by then.  Three barriers.  Out of line: inlined, it pushed the
-// 256-thread form past its 96-register budget (four registers spilled on the common path).
-constexpr int kRank2Factor = 32;
-
+// 256-thread form past its 96-register budget.
 template <int NT, class SH, class Map>
-__device__ __attribute__((noinline)) void rank_by_second_digit(SH& sh, int nc, int kk, int tot_gt,
-                                                               int32_t* __restrict__ out, const Map map) {
+__device__ __attribute__((noinline)) void rank_bucket(SH& sh, int nc, int kk, int tot_gt, int32_t* __restrict__ out,
+                                                      const Map map) {
   using C = Cfg<NT>;
   static_assert(C::Bins >= 256 + 2 * kRankCap, "second-level ranking needs pass 1's histogram words");
   constexpr int S2 = C::Shift - 8;
@@ -443,32 +443,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
     });
     // Rank of each candidate among the bucket by (key desc, index asc); composites are
     // distinct, so the ranks are a permutation of 0..nc-1.
-    if (nc * nc > kRank2Factor * NT) {  // uniform: a large bucket
-      rank_by_second_digit<NT>(sh, nc, kk, tot_gt, out, map);
-      return;
-    }
-    // G adjacent lanes share one candidate (G = NT / nc rounded to a power of two, at
-    // most 64), each counting a strided part of the list, and a lane-xor reduction sums
-    // their counts.
-    int np2 = 1;
-    while (np2 < nc) np2 <<= 1;
-    const int G = max(1, min(64, NT / np2));
-    const int per_sweep = NT / G;
-    for (int base = 0; base < nc; base += per_sweep) {
-      const int c = base + tid / G, part = tid & (G - 1);
-      const uint64_t me = sh.cand[min(c, nc - 1)];
-      int cnt = 0;
-      if (c < nc) {
-        int t = part;
-        for (; t + 7 * G < nc; t += 8 * G) {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) cnt += sh.cand[t + u * G] > me ? 1 : 0;
-        }
-        for (; t < nc; t += G) cnt += sh.cand[t] > me ? 1 : 0;
-      }
-      for (int m = 1; m < G; m <<= 1) cnt += shfl_xor(cnt, m);
-      if (c < nc && part == 0 && cnt < kk) out[tot_gt + cnt] = map.token((int)~(uint32_t)me);
-    }
+    rank_bucket<NT>(sh, nc, kk, tot_gt, out, map);
     return;
   }
 
