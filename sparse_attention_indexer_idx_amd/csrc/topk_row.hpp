@@ -432,15 +432,15 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   int tot_gt, nc, pos_gt, pos_in;
   block_excl_scan2<NT>(n_gt, n_in, sh.wave_tot, pos_gt, pos_in, tot_gt, nc);
   if (nc <= kRankCap) {
+    // One pass: bucket cells to the ranking list, cells above the bucket to their output
+    // slots (a workgroup barrier does not wait for global stores, and the register keys
+    // are dead once it is done, before the ranking).
     for_rounds<EPT>(ne, [&](int e) {
-      if ((key[e] >> C::Shift) == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
+      const uint32_t dg = key[e] >> C::Shift;
+      if (dg == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
+      else if (dg > d1) out[pos_gt++] = map.token(e * NT + tid);
     });
     __syncthreads();
-    // Cells above the bucket: after the last barrier (so no barrier waits for these
-    // stores) and before the ranking (so the register keys are dead while it runs).
-    for_rounds<EPT>(ne, [&](int e) {
-      if ((key[e] >> C::Shift) > d1) out[pos_gt++] = map.token(e * NT + tid);
-    });
     // Rank of each candidate among the bucket by (key desc, index asc); composites are
     // distinct, so the ranks are a permutation of 0..nc-1.
     rank_bucket<NT>(sh, nc, kk, tot_gt, out, map);
