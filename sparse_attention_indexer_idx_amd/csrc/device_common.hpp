@@ -18,7 +18,7 @@ constexpr uint32_t kE8m0One = 0x7F7F7F7Fu;  // every scale byte = 2^0
 
 // Fourth word of a raw buffer descriptor on the gfx9 family (gfx950 included): 32-bit
 // data format, no swizzle; with a zero stride, a load whose offset is at or past the
-// descriptor's byte count returns 0 instead of touching memory.
+// descriptor's byte count returns 0 instead of touching memory, and such a store is dropped.
 constexpr int kBufferRsrcFlags = 0x00020000;
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t h) {

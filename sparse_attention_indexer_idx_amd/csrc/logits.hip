@@ -94,7 +94,7 @@ template <int FMT>
 struct alignas(16) PrefillStage {
   uint4 data[2][kStageTiles][64][FMT == 0 ? 1 : 2];
   uint32_t scale[2][kStageTiles][64];
-  float out[4][kPrefillRowsPerWave][32];  // per wave: two tiles' logits, re-read as pairs
+  float out[4][kPrefillRowsPerWave][64];  // per wave: four tiles' logits, re-read per row
 };
 
 template <int FMT, int HT>
@@ -144,14 +144,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT != 0 ? 
       qw[g][ht] = load_w_tile(a, r, ht, lane);
     }
   }
-  // stores of a tile pair: lane l writes row j0 + 2i + l/32, token l%32
-  float* pair_row[2];
-  int pair_n[2];
+  // One store descriptor per row of the wave, its range the row's valid cells inside this
+  // unit's chunk: a store past it is dropped by the hardware, so no store is conditional.
+  __amdgpu_buffer_rsrc_t orow_rsrc[kPrefillRowsPerWave];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int jr = j0 + 2 * i + (lane >> 5);
-    pair_n[i] = jr < a.n_q ? std::min(valid_len(n_b, a.n_q, jr), t_end) : 0;  // t_end: this unit's chunk
-    pair_row[i] = a.logits + ((int64_t)b * a.n_q + std::min(jr, a.n_q - 1)) * a.lstride;
+  for (int g = 0; g < kPrefillRowsPerWave; ++g) {
+    const int jr = j0 + g;  // uniform
+    const int n_g = jr < a.n_q ? std::min(valid_len(n_b, a.n_q, jr), t_end) : 0;
+    float* row = a.logits + ((int64_t)b * a.n_q + std::min(jr, a.n_q - 1)) * a.lstride;
+    orow_rsrc[g] = __builtin_amdgcn_make_buffer_rsrc(row, 0, n_g * 4, kBufferRsrcFlags);
   }
   const float qnan = __builtin_nanf("");
 
@@ -162,14 +163,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT != 0 ? 
     const bool okk = tile_ok(s0);
     const int32_t pid = __builtin_amdgcn_readlane(win, (std::min(s0, t_end - 1) >> lgP) - page0);
     const uint8_t* page = a.pool.base + (okk ? (int64_t)pid : 0) * a.pool.stride;
-    return load_k_tile<FMT, false>(page, P, okk ? (s0 & (P - 1)) : 0, lane);
+    return load_k_tile_w<FMT, false>(page, P, okk ? (s0 & (P - 1)) : 0, lane);
   };
   auto stash = [&](int buf, int i, const KTile<FMT>& k) {
     const int t = wave * TPW + i;
     st.data[buf][t][lane][0] = make_uint4((uint32_t)k.v[0], (uint32_t)k.v[1], (uint32_t)k.v[2], (uint32_t)k.v[3]);
     if (FMT == 1)
       st.data[buf][t][lane][FMT] = make_uint4((uint32_t)k.v[4], (uint32_t)k.v[5], (uint32_t)k.v[6], (uint32_t)k.v[7]);
-    st.scale[buf][t][lane] = k.scale;
+    st.scale[buf][t][lane] = lane_scale<FMT>(k.scale, lane);
   };
   auto unstash = [&](int buf, int t) {
     KTile<FMT> k;
@@ -185,26 +186,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT != 0 ? 
   };
 
   const int n_groups = (t_end - t_begin + 16 * kStageTiles - 1) / (16 * kStageTiles);
+  // Group gg + 1's tiles are staged at the end of group gg (into the other buffer, whose last
+  // readers passed this group's barrier), so the only loads younger than the ones waited for
+  // there are that group's stores; staged at the loop head, the path from the first fetch
+  // made the compiler wait for every memory operation in flight on each iteration.
   KTile<FMT> nxt[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) nxt[i] = fetch(0, i);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) stash(0, i, nxt[i]);
   for (int gg = 0; gg < n_groups; ++gg) {
     const int buf = gg & 1;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) stash(buf, i, nxt[i]);
-#pragma unroll
     for (int i = 0; i < TPW; ++i) nxt[i] = fetch(gg + 1, i);  // past the end: page 0 row 0, never stashed
     __syncthreads();
-    // Tiles go in pairs: both tiles' logits (lane l: row l/16, token l%16 of each) pass
-    // through the wave's LDS rows and come back as 32 consecutive tokens of two rows per
-    // store, so each store writes two rows' 128-byte runs instead of four half runs.
+    // Tiles go in fours: after the transpose lane l holds row l/16, token l%16 of a tile, and
+    // the four tiles' logits pass through the wave's LDS rows, so each store writes 64
+    // consecutive logits of one row (whole 128-byte lines) instead of a half line of four.
+    // The stores are unconditional buffer stores (cells past a row's valid length fall
+    // outside its descriptor): with stores under a branch, the compiler waited at the next
+    // group's head for every memory operation in flight, these stores included.
 #pragma unroll
-    for (int t = 0; t < kStageTiles; t += 2) {
+    for (int t = 0; t < kStageTiles; t += 4) {
       const int s0 = t_begin + 16 * kStageTiles * gg + 16 * t;
-      if (s0 < t_end) {  // uniform
+      if (s0 < t_end) {  // uniform; tiles of the four past t_end score stale data, never stored
         float* orow = st.out[wave][lane >> 4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 4; ++h) {
           const KTile<FMT> kt = unstash(buf, t + h);
           float p[kPrefillRowsPerWave];
 #pragma unroll
@@ -220,15 +228,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT != 0 ? 
           if (!tile_ok(s0 + 16 * h)) logit = qnan;
           orow[16 * h + (lane & 15)] = logit;
         }
-        __builtin_amdgcn_wave_barrier();  // the reads below take other lanes' writes
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int s = s0 + (lane & 31);
-          const float v = st.out[wave][2 * i + (lane >> 5)][lane & 31];
-          if (s < pair_n[i]) pair_row[i][s] = v;
-        }
-        __builtin_amdgcn_wave_barrier();  // and the next pair's writes come after them
       }
+      __builtin_amdgcn_wave_barrier();  // the reads below take other lanes' writes
+#pragma unroll
+      for (int g = 0; g < kPrefillRowsPerWave; ++g)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st.out[wave][g][lane]), orow_rsrc[g],
+                                              (uint32_t)(s0 + lane) * 4u, 0, 0);
+      __builtin_amdgcn_wave_barrier();  // and the next writes come after them
+    }
+    if (gg + 1 < n_groups) {  // uniform
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) stash(buf ^ 1, i, nxt[i]);
     }
   }
 }

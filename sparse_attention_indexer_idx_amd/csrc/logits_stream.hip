@@ -214,28 +214,19 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
     ok = pid >= 0 && pid < np32;
     return pid;
   };
-  // this wave's tile (t = wave) of chunk cc; past the run it reads page 0 row 0.  MXFP4
-  // loads the token's four E8M0 bytes as one word, shifted to the lane's byte when staged
-  // (a byte load here made the compiler wait for every load in flight at the loop head).
+  // this wave's tile (t = wave) of chunk cc; past the run it reads page 0 row 0
   auto fetch = [&](int cc) {
     bool okk;
     const int32_t pid = page_of(cc, wave, okk);
     const bool use = okk && cc < n_end;
     const uint8_t* page = a.pool.base + (use ? (int64_t)pid : 0) * a.pool.stride;
-    const int row0 = use ? ((64 * cc + 16 * wave) & (P - 1)) : 0;
-    if (FMT == 1) return load_k_tile<FMT, false>(page, P, row0, lane);
-    KTile<FMT> k;
-    const uint32_t tok = (uint32_t)(row0 + (lane & 15));
-    const u32x4 x = *(const u32x4*)(page + (tok * 64u + 16u * (uint32_t)(lane >> 4)));
-    k.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-    k.scale = *(const uint32_t*)(page + ((uint32_t)P * 64u + tok * 4u));
-    return k;
+    return load_k_tile_w<FMT, false>(page, P, use ? ((64 * cc + 16 * wave) & (P - 1)) : 0, lane);
   };
   auto stash = [&](int buf, const KTile<FMT>& k) {
     st.data[buf][wave][lane][0] = make_uint4((uint32_t)k.v[0], (uint32_t)k.v[1], (uint32_t)k.v[2], (uint32_t)k.v[3]);
     if (FMT == 1)
       st.data[buf][wave][lane][FMT] = make_uint4((uint32_t)k.v[4], (uint32_t)k.v[5], (uint32_t)k.v[6], (uint32_t)k.v[7]);
-    st.scale[buf][wave][lane] = FMT == 0 ? k.scale >> (8 * (lane >> 4)) : k.scale;
+    st.scale[buf][wave][lane] = lane_scale<FMT>(k.scale, lane);
   };
   auto unstash = [&](int buf, int t) {
     KTile<FMT> k;
@@ -288,12 +279,16 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
   }
 }
 
+// The one-row form loads MXFP4 K non-temporally (read once per call).  An FP8 token row spans
+// two 64-byte halves of a line, fetched by separate loads, and cacheable loads let the second
+// half find the line the first brought in: large pool 81.5 -> 78 us, while MXFP4 measured 11 %
+// slower with cacheable loads.
 template <int FMT, int M>
 hipError_t launch_stream_m(const LogitsArgs& a, dim3 grid, int ht, hipStream_t s) {
   switch (ht) {
 #define IDX_STREAM_CASE(N) \
   case N: \
-    if (a.n_q == 1) hipLaunchKernelGGL((logits_stream_kernel<FMT, N, true, M>), grid, dim3(256), 0, s, a); \
+    if (a.n_q == 1) hipLaunchKernelGGL((logits_stream_kernel<FMT, N, FMT == 0, M>), grid, dim3(256), 0, s, a); \
     else hipLaunchKernelGGL((logits_stream_rows_kernel<FMT, N, M>), grid, dim3(256), 0, s, a); \
     break;
     IDX_STREAM_CASE(1) IDX_STREAM_CASE(2) IDX_STREAM_CASE(3) IDX_STREAM_CASE(4)

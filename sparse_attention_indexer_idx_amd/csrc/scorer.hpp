@@ -66,6 +66,24 @@ __device__ __forceinline__ KTile<FMT> load_k_tile(const uint8_t* __restrict__ pa
   return t;
 }
 
+// As load_k_tile, but an MXFP4 tile's E8M0 scales come as each token's four bytes in one
+// word, which lane_scale shifts to the lane's byte (the MFMA reads the low byte): in a loop, a
+// byte load made the compiler wait for every memory operation in flight at the loop head.
+template <int FMT, bool STREAM>
+__device__ __forceinline__ KTile<FMT> load_k_tile_w(const uint8_t* __restrict__ page, int P, int row0, int lane) {
+  if (FMT == 1) return load_k_tile<FMT, STREAM>(page, P, row0, lane);
+  KTile<FMT> t;
+  const uint32_t tok = (uint32_t)(row0 + (lane & 15)), g = (uint32_t)(lane >> 4);
+  const u32x4 x = ld<STREAM>((const u32x4*)(page + (tok * 64u + 16u * g)));
+  t.v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  t.scale = ld<STREAM>((const uint32_t*)(page + ((uint32_t)P * 64u + tok * 4u)));
+  return t;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t lane_scale(uint32_t w, int lane) {
+  return FMT == 0 ? w >> (8 * (lane >> 4)) : w;
+}
+
 // A operand for head tile `ht` of query row r: lane l -> head ht*16 + l%16, block l/16.
 // Branch-free: a head past H loads head H-1 and is zeroed by a select after the load, so
 // the loads of every tile go out together and nothing waits for them before first use.
@@ -162,9 +180,12 @@ struct NoPatch {
 // j_base = 0 and NT = n_q * HT; one row when NT = HT).  EXIT_DEAD: a wave wholly past its
 // sequence leaves before its K loads (worth it where many waves are: many heads and mixed
 // lengths); the price is that the compiler then issues the Q loads after the page-table
-// round trip instead of before it, so the single-row decode kernel does without.  STREAM_K: K loads are non-temporal (read once per
-// call); off where several waves read the same tiles from the cache.
-template <int FMT, int NT, int G, class Patch, bool EXIT_DEAD = false, bool STREAM_K = true>
+// round trip instead of before it, so the single-row decode kernel does without.
+// STREAM_K: K loads are non-temporal (read once per call).  By default on for MXFP4 only: an
+// FP8 token row is two 64-byte halves of a line fetched by separate loads, and cacheable
+// loads let the second find the line the first brought in (fused decode step, B64/H32/8K
+// FP8: 23.8 -> 22.3 us); off too where several waves read the same tiles from the cache.
+template <int FMT, int NT, int G, class Patch, bool EXIT_DEAD = false, bool STREAM_K = (FMT == 0)>
 __device__ __forceinline__ void decode_wave(const LogitsArgs& a, int b, int tok0, int lane, Patch& patch,
                                             int j_base = 0) {
   constexpr int T = 4 * G;  // K tiles per wave
