@@ -8,12 +8,13 @@
 // one sequence (sequence b gets ceil(chunks_b / q) workers), so long and short sequences
 // finish together and a worker's query tiles stay the same throughout its run.  Each wave
 // computes U, q and its own run from the lengths (a wave-wide prefix over the sequences).
-// A worker is a wave when n_q = 1; for n_q = 2..4 it is a block whose wave j scores query
-// row j of the same chunks, so the rows of a chunk run on one CU and all but one read its
-// K from the cache.  Within a run, the next chunk's K tiles are in flight while the
-// current one is scored (two register buffers used alternately); loads are issued on every
-// step, past the run too (page 0 row 0), so the outstanding-load count is the same on every
-// path.
+// A worker is a wave when n_q = 1; for n_q = 2..4 it is a block whose four waves stage a
+// chunk's K tiles in LDS and whose wave j scores query row j from them, so a chunk's K
+// leaves HBM once per block.  A run's page ids are loaded once (RunPages), and the launch
+// caps the run length so that they fit its 64-entry window.  Within a run, the next chunks'
+// K tiles are in flight while the current one is scored (register buffers used
+// alternately); loads are issued on every step, past the run too (page 0 row 0), so the
+// outstanding-load count is the same on every path and the compiler's waits stay partial.
 #include <algorithm>
 
 #include "scorer.hpp"
