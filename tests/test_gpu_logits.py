@@ -123,6 +123,9 @@ def edge_workload(H, n_q, P, ctx, fmt=wl.MXFP4):
     (32, 33, 128, [40, 1000], wl.FP8),         # the same in FP8
     (20, 17, 64, [17, 700, 0], wl.FP8),        # FP8 prefill, ragged head tile, an empty sequence
     (128, 5, 64, [300], wl.MXFP4),             # prefill form with 8 head tiles
+    (16, 40, 64, [2500, 50], wl.MXFP4),        # prefill, one head tile, rows crossing the 1024-token chunks
+    (48, 24, 32, [2100, 700], wl.MXFP4),       # prefill, three head tiles, 32-token pages
+    (32, 40, 128, [2500, 1030], wl.FP8),       # FP8 prefill across chunk edges
 ])
 def test_logits_shapes_and_edges(H, n_q, P, ctx, fmt):
     W = edge_workload(H, n_q, P, ctx, fmt)
