@@ -206,3 +206,46 @@ def test_logits_streaming_many_sequences(n_q, fmt):
     d = setup_scorer(W, fmt)
     logits = run_scorer(W, d, stride=W.max_ctx + 3)
     check(W, d, logits, np.arange(W.rows), f"stream 150 seqs nq{n_q}/fmt{fmt}")
+
+
+@pytest.mark.parametrize("form,H,n_q,P,ctx,fmt", [
+    ("prefill", 32, 40, 128, [2500, 1030], wl.MXFP4),
+    ("stream", 32, 1, 128, [140000, 100, 3000, 64, 1, 0, 5000, 77, 9, 650, 2048, 64, 63, 65, 1000, 17], wl.MXFP4),
+    ("stream", 32, 1, 128, [140000, 100, 3000, 64, 1, 0, 5000, 77, 9, 650, 2048, 64, 63, 65, 1000, 17], wl.FP8),
+])
+def test_scorer_graph_replay_matches_eager(form, H, n_q, P, ctx, fmt):
+    """The prefill form (its unit table built on the host at capture) and the one-row
+    streaming form (its runs computed on the device from the lengths) captured in a HIP
+    graph: every replay, with eager work and a synchronisation between replays, writes the
+    eager call's logits bit for bit."""
+    torch = G.torch_cuda()
+    W = edge_workload(H, n_q, P, ctx, fmt)
+    G.say(f"scorer graph replay form={form} fmt={fmt}")
+    d = setup_scorer(W, fmt)
+    sentinel = np.int32(np.uint32(G.SENTINEL_BITS).view(np.int32))
+    logits = torch.empty((W.rows, W.max_ctx + 3), dtype=torch.float32, device="cuda")
+
+    def call():
+        bd.idx_logits_paged(d["pool"].view, d["q_d"], d["qs_d"], d["w_d"], d["pt_d"], d["ctx_d"], W.B, W.n_q, W.H,
+                            W.max_ctx, logits)
+
+    logits.view(torch.int32).fill_(sentinel)
+    call()
+    torch.cuda.synchronize()
+    ref = logits.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        logits.view(torch.int32).fill_(sentinel)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
+    if form == "stream":  # and every row against the oracle (this shape is not covered elsewhere)
+        check(W, d, logits, np.arange(W.rows), f"graph {form}/fmt{fmt}")
