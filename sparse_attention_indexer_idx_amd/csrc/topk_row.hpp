@@ -121,12 +121,13 @@ __device__ __forceinline__ void block_excl_scan2(int v0, int v1, int32_t* wave_t
 }
 
 // Given a histogram of BINS digits (BINS >= NT), find the digit d holding the kk-th
-// largest item (kk >= 1): count(digits > d) < kk <= count(digits >= d).  Thread t covers
+// largest item (kk >= 1): count(digits > d) < kk <= count(digits >= d), with the whole
+// block (the form for 1024-thread rows, where it measured faster).  Thread t covers
 // BINS/NT consecutive digits, the highest to thread 0, read as 16-byte words and kept in
 // registers; only the thread whose range holds the answer walks its bins.  Leaves d and
 // count(> d) in shared memory (two barriers).
 template <int NT, int BINS, class SH>
-__device__ __forceinline__ void select_digit(SH& sh, int kk) {
+__device__ __forceinline__ void select_digit_block(SH& sh, int kk) {
   constexpr int PER = BINS / NT;
   const int lo = BINS - PER * ((int)threadIdx.x + 1);  // digits [lo, lo + PER)
   uint32_t c[PER];
@@ -160,6 +161,65 @@ __device__ __forceinline__ void select_digit(SH& sh, int kk) {
     }
   }
   __syncthreads();
+}
+
+// The same with wave 0 alone, the form for the smaller blocks, which share a CU several at
+// a time (prefill top-k 49 -> 47 us; 1024-thread rows measured slower with it).  Lane l
+// sums the BINS/64 consecutive digits [lo, lo + BINS/64) with lo = BINS - (l + 1) *
+// BINS/64 (the highest digits to lane 0), reading its 16-byte words in an order rotated by
+// the lane so that one read instruction spreads over the LDS banks (in digit order every
+// lane would hit the same banks); a wave scan finds the lane whose range holds the kk-th
+// item, and a second scan over that range's digits, at most two per lane, finds the digit.
+// Requires kk <= the histogram's total.  Leaves d and count(> d) in shared memory; one
+// barrier.
+template <int NT, int BINS, class SH>
+__device__ __forceinline__ void select_digit_wave(SH& sh, int kk) {
+  static_assert(BINS == 1024 || BINS == 4096 || BINS == 8192, "16, 64 or 128 digits per lane");
+  constexpr int PER = BINS / 64;               // digits per lane
+  constexpr int Q = PER / 4;                   // 16-byte words per lane
+  constexpr int P2 = PER >= 64 ? PER / 64 : 1;  // digits per lane in the second scan
+  constexpr int N2 = PER / P2;                 // lanes in the second scan
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int lo = BINS - PER * (lane + 1);
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(sh.hist + lo)[(q + lane) & (Q - 1)];
+      local += (int)(v.x + v.y + v.z + v.w);
+    }
+    const int incl = wave_incl_scan(local);
+    const int before = incl - local;
+    const uint64_t own = __ballot(before < kk && kk <= incl);  // exactly one lane
+    const int L = own ? __builtin_ctzll(own) : 0;
+    const int base = __builtin_amdgcn_readlane(before, L);
+    const int lo2 = BINS - PER * (L + 1) + PER - P2 * (lane + 1);  // lane's digits in L's range
+    int cnt[P2], c2 = 0;
+#pragma unroll
+    for (int q = 0; q < P2; ++q) {
+      cnt[q] = lane < N2 ? (int)sh.hist[lo2 + q] : 0;
+      c2 += cnt[q];
+    }
+    const int incl2 = wave_incl_scan(c2);
+    int b = base + incl2 - c2;
+    if (b < kk && kk <= b + c2) {  // one lane: walk its digits from the highest
+#pragma unroll
+      for (int q = P2 - 1; q >= 0; --q) {
+        if (b < kk && kk <= b + cnt[q]) {
+          sh.sel_digit = lo2 + q;
+          sh.sel_above = b;
+        }
+        b += cnt[q];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int NT, int BINS, class SH>
+__device__ __forceinline__ void select_digit(SH& sh, int kk) {
+  if constexpr (NT >= 1024) select_digit_block<NT, BINS>(sh, kk);
+  else select_digit_wave<NT, BINS>(sh, kk);
 }
 
 // Runs f(e) for every round e < EPT whose group of 8 rounds holds a valid cell: a group
