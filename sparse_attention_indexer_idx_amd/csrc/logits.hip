@@ -82,12 +82,14 @@ struct PrefillPlan {
 
 
 // Prefill form with the K tiles shared through LDS: the four waves of a block score the
-// same tokens for different rows, so each group of four 16-token tiles is fetched once
-// per block (wave w fetches tile w into registers, then LDS; lane l of every wave reads
-// back the operand lane l fetched, which is its own MFMA operand for that tile).  Two LDS
-// buffers alternate, with one barrier per group; the next group's fetch is in flight
-// while the current one is scored.  Block-uniform token range (the block's last row), so
-// every wave runs the same number of groups.
+// same tokens for different rows, so each group of eight 16-token tiles is fetched once
+// per block (wave w fetches tiles 2w and 2w + 1 into registers, then LDS; lane l of every
+// wave reads back the operand lane l fetched, which is its own MFMA operand for that
+// tile).  Two LDS buffers alternate, with one barrier per group; the next group's fetch is
+// in flight while the current one is scored.  Block-uniform token range (the block's last
+// row), so every wave runs the same number of groups.  The occupancy targets hold the
+// MXFP4 forms with one and two head tiles at their register budgets (six and four waves
+// per SIMD).
 constexpr int kStageTiles = 8;  // tiles per group: kStageTiles / 4 per wave
 
 template <int FMT>
@@ -98,8 +100,9 @@ struct alignas(16) PrefillStage {
 };
 
 template <int FMT, int HT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT != 0 ? 1 : HT == 1 ? 6 : HT == 2 ? 4 : 1))) void logits_prefill_kernel(
-    LogitsArgs a, PrefillPlan plan) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(FMT != 0 ? 1 : HT == 1 ? 6 : HT == 2 ? 4 : 1)))
+void logits_prefill_kernel(LogitsArgs a, PrefillPlan plan) {
   __shared__ PrefillStage<FMT> st;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);

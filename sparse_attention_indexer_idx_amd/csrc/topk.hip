@@ -11,8 +11,8 @@ namespace {
 // then start first instead of forming a tail.  The 256-thread form (many rows per CU) is
 // held to 96 registers, five waves per SIMD instead of four (it fits without spills).
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 && EPT <= 32 ? 5 : 1))) void topk_kernel(
-    TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 && EPT <= 32 ? 5 : 1)))
+void topk_kernel(TopkArgs a) {
   __shared__ TopkShared<NT, EPT> sh;
   const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int b = (int)(r / a.n_q), j = (int)(r % a.n_q);
