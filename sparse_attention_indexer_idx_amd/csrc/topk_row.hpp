@@ -272,8 +272,8 @@ struct CandidateRow {
 // exact rank, and so the output slot, at a cost of the run length per candidate instead of
 // the bucket size.  (Measured against ranking over the whole bucket with lane groups sharing
 // a candidate: as fast or faster at every bucket size of the benchmark rows.)  The 256
-// counters follow pass 1's bins (cleared with them); the run ends and the sorted list reuse
-// pass 1's words, dead by then.  Three barriers.  Out of line: inlined, it pushed the
+// counters follow pass 1's bins (cleared with them); the run starts and the sorted list
+// reuse pass 1's words, dead by then.  Three barriers.  Out of line: inlined, it pushed the
 // 256-thread form past its 96-register budget.
 template <int NT, class SH, class Map>
 __device__ __attribute__((noinline)) void rank_bucket(SH& sh, int nc, int kk, int tot_gt, int32_t* __restrict__ out,
@@ -283,26 +283,42 @@ __device__ __attribute__((noinline)) void rank_bucket(SH& sh, int nc, int kk, in
   constexpr int S2 = C::Shift - 8;
   const int tid = threadIdx.x;
   uint32_t* cnt = sh.hist + C::Bins;  // per second digit: candidates
-  uint32_t* end = sh.hist;            // per second digit: end of its run (a cursor while sorting)
+  uint32_t* start = sh.hist;          // per second digit: start of its run in the sorted list
   uint64_t* sorted = reinterpret_cast<uint64_t*>(sh.hist + 256);
   auto digit2 = [](uint64_t c) { return (uint32_t)(c >> (32 + S2)) & 255u; };
-  for (int i = tid; i < nc; i += NT) atomicAdd(&cnt[digit2(sh.cand[i])], 1u);
+  // Each candidate's place within its digit's run comes back from its counter's atomic.
+  constexpr int PER = (kRankCap + NT - 1) / NT;
+  uint32_t place[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + q * NT;
+    if (i < nc) place[q] = atomicAdd(&cnt[digit2(sh.cand[i])], 1u);
+  }
   __syncthreads();
-  // start of each digit's run: the candidates of higher digits (thread t holds digit 255 - t)
-  const int v = tid < 256 ? (int)cnt[255 - tid] : 0;
-  int total;
-  const int before = block_excl_scan<NT>(v, sh.wave_tot, total);
-  if (tid < 256) end[255 - tid] = (uint32_t)before;
+  // Start of each digit's run: the candidates of higher digits.  Wave 0 alone: lane l
+  // holds digits 255 - 4l - 3 .. 255 - 4l, read as one 16-byte word.
+  if (tid < 64) {
+    const uint4 c4 = reinterpret_cast<const uint4*>(cnt)[63 - tid];  // digits 252 - 4l .. 255 - 4l
+    const int local = (int)(c4.x + c4.y + c4.z + c4.w);
+    const int before = wave_incl_scan(local) - local;
+    reinterpret_cast<uint4*>(start)[63 - tid] =
+        make_uint4((uint32_t)before + c4.w + c4.z + c4.y, (uint32_t)before + c4.w + c4.z, (uint32_t)before + c4.w,
+                   (uint32_t)before);
+  }
   __syncthreads();
-  for (int i = tid; i < nc; i += NT) {
-    const uint64_t c = sh.cand[i];
-    sorted[atomicAdd(&end[digit2(c)], 1u)] = c;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + q * NT;
+    if (i < nc) {
+      const uint64_t c = sh.cand[i];
+      sorted[start[digit2(c)] + place[q]] = c;
+    }
   }
   __syncthreads();
   for (int j = tid; j < nc; j += NT) {
     const uint64_t me = sorted[j];
     const uint32_t d = digit2(me);
-    const int hi = (int)end[d], lo = hi - (int)cnt[d];
+    const int lo = (int)start[d], hi = lo + (int)cnt[d];
     int rank = lo;
     for (int i = lo; i < hi; ++i) rank += sorted[i] > me ? 1 : 0;
     if (rank < kk) out[tot_gt + rank] = map.token((int)~(uint32_t)me);
