@@ -511,11 +511,13 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
     // One pass: bucket cells to the ranking list, cells above the bucket to their output
     // slots (a workgroup barrier does not wait for global stores, and the register keys
     // are dead once it is done, before the ranking).  In a dense row every lane stores
-    // every round, through a descriptor covering the k output slots: a lane whose cell is
-    // not above the bucket stores past it, which the hardware drops, so the loop carries no
+    // every round, through a descriptor covering the slots those cells can take: a lane
+    // whose cell is not above the bucket stores past it, which the hardware drops (and no
+    // offset overflows for any k), so the loop carries no
     // branch on the (mostly mixed) per-lane selection.  Bucket cells are few, and their
     // branch is skipped whole by most rounds.
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, k * 4, kBufferRsrcFlags);
+    const int obytes = min(k, n) * 4;  // the slots of cells above the bucket lie below min(k, n)
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, obytes, kBufferRsrcFlags);
     for_rounds<EPT>(ne, [&](int e) {
       const uint32_t dg = key[e] >> C::Shift;
       if (dg == d1) sh.cand[pos_in++] = ((uint64_t)key[e] << 32) | (uint32_t)~(e * NT + tid);
@@ -523,7 +525,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
         if (dg > d1) out[pos_gt++] = map.token(e * NT + tid);
       } else {
         const bool above = dg > d1;
-        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)map.token(e * NT + tid), orsrc, above ? pos_gt * 4 : k * 4,
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)map.token(e * NT + tid), orsrc, above ? pos_gt * 4 : obytes,
                                               0, 0);
         pos_gt += above ? 1 : 0;
       }

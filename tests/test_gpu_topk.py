@@ -40,6 +40,7 @@ def gpu_topk(logits_d, ctx, B, n_q, k):
     (2100, 1, (1, 8192), 1024, True),        # many rows, heavy ties
     (2600, 2, (900, 5000), 300, False),      # many rows, n_q 2, small k
     (2048, 1, (16000, 16384), 1024, True),   # many long rows with ties
+    (64, 1, (2000, 8192), 3000, False),      # a large k, some rows shorter than it
 ])
 def test_topk_isolated_exact(rows, n_q, lens, k, ties):
     rng = np.random.default_rng(rows * 7 + k + int(ties))
