@@ -512,10 +512,10 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
     // slots (a workgroup barrier does not wait for global stores, and the register keys
     // are dead once it is done, before the ranking).  In a dense row every lane stores
     // every round, through a descriptor covering the slots those cells can take: a lane
-    // whose cell is not above the bucket stores past it, which the hardware drops (and no
-    // offset overflows for any k), so the loop carries no
-    // branch on the (mostly mixed) per-lane selection.  Bucket cells are few, and their
-    // branch is skipped whole by most rounds.
+    // whose cell is not above the bucket stores past it, which the hardware drops (no
+    // offset overflows for any k), so the loop carries no branch on the (mostly mixed)
+    // per-lane selection.  Bucket cells are few, and their branch is skipped whole by
+    // most rounds.
     const int obytes = min(k, n) * 4;  // the slots of cells above the bucket lie below min(k, n)
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, obytes, kBufferRsrcFlags);
     for_rounds<EPT>(ne, [&](int e) {
