@@ -12,7 +12,9 @@
 // block then publishes its logits (device-coherent stores) and counts itself in on the
 // sequence's counter; the last block of a sequence invalidates its caches once and runs
 // the top-k of the sequence's rows with all 1024 threads (topk_row.hpp), then resets the
-// counter.
+// counter.  When B is a multiple of the XCD count, the blocks of one sequence run on one
+// XCD, so its query tiles are fetched into one L2 and its last block finds its siblings'
+// logits nearer (fused step 15.9 -> 15.6 us at decode B64/H32/8K).
 #include "kstore_row.hpp"
 #include "scorer.hpp"
 #include "topk_row.hpp"
@@ -29,6 +31,9 @@ constexpr int kStepTok = kStepWaves * 64 * kStepG;
 constexpr int kStepMaxTiles = 2;
 constexpr int kStepMaxCtx = 16 * 1024;
 constexpr int kRowWords = 33;   // one K row in page layout: 16 (or 32) data words, then the scale word
+constexpr int kXcds = 8;        // XCDs of the device (a power of two)
+
+__host__ __device__ __forceinline__ int step_chunks(int max_ctx) { return (max_ctx + kStepTok - 1) / kStepTok; }
 
 // The step's new K rows.  prepare(): every wave of the block learns which of the newest
 // n_q tokens fall in the block and have a row to store (valid slot and position); the
@@ -104,8 +109,21 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
   __shared__ int last;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  const int blk0 = blockIdx.x * kStepTok;
+  // Linear block ids are dispatched round-robin over the XCDs, each with its own L2.  When
+  // B is a multiple of their count, sequence b takes C slots of XCD b % kXcds (its query
+  // tiles fetched into one L2, its logits written and re-read in one place); otherwise the
+  // blocks go in sequence order, as an uneven split would leave XCDs short of work.
+  const int C = step_chunks(a.s.max_ctx);
+  int b, blk0;
+  if (a.s.B % kXcds == 0) {
+    const int x = (int)blockIdx.x & (kXcds - 1), slot = (int)blockIdx.x / kXcds;
+    b = (slot / C) * kXcds + x;
+    blk0 = (slot % C) * kStepTok;
+  } else {
+    b = (int)blockIdx.x / C;
+    blk0 = ((int)blockIdx.x % C) * kStepTok;
+  }
+  if (b >= a.s.B) return;
   const int tok0 = blk0 + wave * (64 * kStepG);
   NewRows<FMT, NT> nr{&a, b, blk0, wave == 0, row_buf, {}};
   decode_wave<FMT, NT, kStepG>(a.s, b, tok0, lane, nr);
@@ -120,7 +138,7 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const int done = __hip_atomic_fetch_add(&a.counters[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = done == (int)gridDim.x - 1;
+    last = done == C - 1;
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
@@ -162,13 +180,13 @@ bool decode_step_supported(int n_q, int H, int64_t max_ctx) {
 }
 
 bool decode_step_fuses(int B, int n_q, int H, int max_ctx, int num_cus) {
-  const int64_t blocks = (int64_t)((max_ctx + kStepTok - 1) / kStepTok) * B;
+  const int64_t blocks = (int64_t)step_chunks(max_ctx) * B;
   const int nt = n_q * ((H + kHeadTile - 1) / kHeadTile);
   return max_ctx > 0 && blocks <= num_cus && nt <= kStepMaxTiles && max_ctx <= kStepMaxCtx;
 }
 
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t s, int num_cus) {
-  const dim3 grid((unsigned)((a.s.max_ctx + kStepTok - 1) / kStepTok), (unsigned)a.s.B);
+  const dim3 grid((unsigned)((int64_t)a.s.B * step_chunks(a.s.max_ctx)));
   const int nt = a.s.n_q * ((a.s.H + kHeadTile - 1) / kHeadTile);
   if (!decode_step_fuses(a.s.B, a.s.n_q, a.s.H, a.s.max_ctx, num_cus)) {
     // More blocks than CUs (a 1024-thread block per CU leaves the scorer short of waves in
