@@ -25,8 +25,13 @@ namespace {
 constexpr int kStreamMaxSeqs = 64 * 16;  // sequences a wave's prefix covers (16 per lane)
 
 // The worker's run: sequence b and chunks [c0, c1) (c0 >= c1: no work).  Every lane of
-// the wave gets the same values.  Lane l holds sequences [l*m, l*m + m).
-template <int M>
+// the wave gets the same values.  Lane l holds sequences [l*m, l*m + m).  Worker w is wave
+// w % WPB of block w / WPB.  The device hands linear block ids to its kXcds XCDs in turn;
+// when the block count is a multiple of kXcds, XCD x takes the runs [x*per, (x+1)*per) in
+// order (per: the busy runs over kXcds, in whole blocks), so the runs of one sequence mostly
+// share one L2 and its query tiles are fetched there once.
+constexpr int kXcds = 8;
+template <int M, int WPB>
 __device__ __forceinline__ void worker_run(const LogitsArgs& a, int worker, int n_workers, int lane, int& b, int& c0,
                                            int& c1) {
   int ch[M];
@@ -46,6 +51,12 @@ __device__ __forceinline__ void worker_run(const LogitsArgs& a, int worker, int 
   for (int i = 0; i < M; ++i) wsum += (ch[i] + q - 1) / q;
   const int wincl = wave_incl_scan(wsum);
   const int wexcl = wincl - wsum;
+  if ((n_workers / WPB) % kXcds == 0) {
+    const int busy = __builtin_amdgcn_readlane(wincl, 63);  // runs with work
+    const int per = WPB * ((busy + WPB * kXcds - 1) / (WPB * kXcds));
+    const int blk = worker / WPB, slot = blk / kXcds;
+    worker = slot * WPB < per ? (blk % kXcds) * per + slot * WPB + worker % WPB : busy;  // busy: no run
+  }
   const uint64_t hit = __ballot(wexcl <= worker && worker < wincl);
   b = -1;
   c0 = c1 = 0;
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(256) void logits_stream_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   int b, c, c_end;
-  worker_run<M>(a, blockIdx.x * 4 + wave, gridDim.x * 4, lane, b, c, c_end);
+  worker_run<M, 4>(a, blockIdx.x * 4 + wave, gridDim.x * 4, lane, b, c, c_end);
   if (b < 0 || c >= c_end) return;  // uniform: no run for this worker
   const int64_t r = b;  // one query row per sequence
   const int P = a.pool.page_size, lgP = a.pool.page_shift;
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(256) void logits_stream_rows_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   int b, c0, c_end;
-  worker_run<M>(a, blockIdx.x, gridDim.x, lane, b, c0, c_end);
+  worker_run<M, 1>(a, blockIdx.x, gridDim.x, lane, b, c0, c_end);
   if (b < 0 || c0 >= c_end) return;  // block-uniform: no run for this worker
   const int j = std::min(wave, a.n_q - 1);  // waves past n_q fetch but do not score
   const bool scorer = wave < a.n_q;
