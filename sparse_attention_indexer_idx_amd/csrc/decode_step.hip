@@ -31,7 +31,6 @@ constexpr int kStepTok = kStepWaves * 64 * kStepG;
 constexpr int kStepMaxTiles = 2;
 constexpr int kStepMaxCtx = 16 * 1024;
 constexpr int kRowWords = 33;   // one K row in page layout: 16 (or 32) data words, then the scale word
-constexpr int kXcds = 8;        // XCDs of the device (a power of two)
 
 __host__ __device__ __forceinline__ int step_chunks(int max_ctx) { return (max_ctx + kStepTok - 1) / kStepTok; }
 

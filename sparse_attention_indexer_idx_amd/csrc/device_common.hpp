@@ -16,6 +16,11 @@ constexpr int kMfmaFmtFp8 = 0;  // OCP e4m3
 constexpr int kMfmaFmtFp4 = 4;  // E2M1
 constexpr uint32_t kE8m0One = 0x7F7F7F7Fu;  // every scale byte = 2^0
 
+// XCDs of an MI355X.  The device hands the linear block ids of a launch to its XCDs in turn
+// (block n to XCD n % kXcds), and each XCD has its own L2, so kernels whose blocks share
+// inputs lay their work out per XCD.  A power of two.
+constexpr int kXcds = 8;
+
 // Fourth word of a raw buffer descriptor on the gfx9 family (gfx950 included): 32-bit
 // data format, no swizzle; with a zero stride, a load whose offset is at or past the
 // descriptor's byte count returns 0 instead of touching memory, and such a store is dropped.

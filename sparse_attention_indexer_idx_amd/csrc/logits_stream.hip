@@ -26,11 +26,9 @@ constexpr int kStreamMaxSeqs = 64 * 16;  // sequences a wave's prefix covers (16
 
 // The worker's run: sequence b and chunks [c0, c1) (c0 >= c1: no work).  Every lane of
 // the wave gets the same values.  Lane l holds sequences [l*m, l*m + m).  Worker w is wave
-// w % WPB of block w / WPB.  The device hands linear block ids to its kXcds XCDs in turn;
-// when the block count is a multiple of kXcds, XCD x takes the runs [x*per, (x+1)*per) in
-// order (per: the busy runs over kXcds, in whole blocks), so the runs of one sequence mostly
-// share one L2 and its query tiles are fetched there once.
-constexpr int kXcds = 8;
+// w % WPB of block w / WPB.  When the block count is a multiple of kXcds, XCD x takes the
+// runs [x*per, (x+1)*per) in order (per: the busy runs over kXcds, in whole blocks), so the
+// runs of one sequence mostly share one L2 and its query tiles are fetched there once.
 template <int M, int WPB>
 __device__ __forceinline__ void worker_run(const LogitsArgs& a, int worker, int n_workers, int lane, int& b, int& c0,
                                            int& c1) {
