@@ -208,6 +208,21 @@ def test_step_edges():
     compare_paths(W, wl.MXFP4, ctx=ctx, slot_override=pad, label="edges")
 
 
+@pytest.mark.parametrize("cfg,scale", [(1, {"B": 16}), (4, {"B": 24})])
+def test_step_xcd_grouped_mixed_lengths(cfg, scale):
+    """B a multiple of the XCD count, so the fused kernel places a sequence's blocks on one
+    XCD (its grouped block order), with mixed lengths down to one token, so sequences end
+    in different chunks and some chunks are empty: 16 sequences of up to 8192 tokens (4
+    chunks), 24 of up to 16384 (8 chunks, 192 blocks)."""
+    W = wl.make_workload(cfg, scale=scale)
+    assert W.B % 8 == 0 and bd.idx_decode_step_fused(W.B, W.n_q, W.H, W.max_ctx) == 1
+    rng = np.random.default_rng(70 + W.B)
+    ctx = np.array([rng.integers(1, int(c) + 1) for c in W.ctx], np.int32)
+    ctx[0], ctx[-1] = 1, W.ctx[-1]
+    G.say(f"decode step, grouped block order, cfg={cfg} B={W.B}")
+    compare_paths(W, wl.MXFP4, ctx=ctx, label=f"grouped cfg{cfg} B{W.B}")
+
+
 @pytest.mark.parametrize("cfg,scale", [(1, {"B": 6}), (4, {"B": 40})])
 def test_step_skips_rows_before_the_first_token(cfg, scale):
     """A row whose token index ctx[b] - n_q + j is negative is not stored even with a
