@@ -19,7 +19,8 @@ void topk_kernel(TopkArgs a) {
   const int n_b = min(max(a.ctx[b], 0), a.max_ctx);
   int n = n_b - a.n_q + 1 + j;
   n = n < 0 ? 0 : (n > n_b ? n_b : n);
-  topk_row<NT, EPT>(a.logits + r * a.lstride, n, a.k, a.out + r * a.k, sh);
+  if constexpr (EPT > 32) topk_row_stream<NT, EPT>(a.logits + r * a.lstride, n, a.k, a.out + r * a.k, sh);
+  else topk_row<NT, EPT>(a.logits + r * a.lstride, n, a.k, a.out + r * a.k, sh);
 }
 
 // Candidate rows: n_cand*P cells, -inf cells are not candidates, cells map to tokens
@@ -31,8 +32,12 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(TopkCandArgs a) {
   CandidateRow map;
   map.cand = a.cand + r * a.n_cand;
   map.page_shift = a.page_shift;
-  topk_row<NT, EPT, CandidateRow>(a.logits + r * a.lstride, a.n_cand << a.page_shift, a.k, a.out + r * a.k, sh,
-                                  map);
+  if constexpr (EPT > 32)
+    topk_row_stream<NT, EPT, CandidateRow>(a.logits + r * a.lstride, a.n_cand << a.page_shift, a.k, a.out + r * a.k,
+                                           sh, map);
+  else
+    topk_row<NT, EPT, CandidateRow>(a.logits + r * a.lstride, a.n_cand << a.page_shift, a.k, a.out + r * a.k, sh,
+                                    map);
 }
 
 template <int NT>

@@ -237,6 +237,31 @@ __device__ __forceinline__ void for_rounds(int ne, F&& f) {
   }
 }
 
+// Runs f(e, load(e)) for every round e < EPT, in groups of 8 rounds with the next group's
+// loads in flight while the current one is used: two register sets used alternately, in a
+// loop kept rolled (unrolled, the compiler hoisted every load and spilled), so no register
+// copy waits on a load.  No branch on the row's length: a load past the row reads 0 (buffer
+// range check), which the callers mask to key 0.
+template <int EPT, class L, class F>
+__device__ __forceinline__ void stream_rounds(L&& load, F&& f) {
+  constexpr int G = 8;  // groups of 16 measured slower (65536-cell rows: 27.1 against 25.1 us)
+  static_assert(EPT % (2 * G) == 0, "whole pairs of groups");
+  float A[G], B[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) A[i] = load(i);
+#pragma unroll 1
+  for (int g = 0; g < EPT; g += 2 * G) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) B[i] = load(g + G + i);
+#pragma unroll
+    for (int i = 0; i < G; ++i) f(g + i, A[i]);
+#pragma unroll
+    for (int i = 0; i < G; ++i) A[i] = load(g + 2 * G + i);  // past EPT on the last pair: reads 0, unused
+#pragma unroll
+    for (int i = 0; i < G; ++i) f(g + G + i, B[i]);
+  }
+}
+
 // How a row's cells become keys and output indices.  DenseRow: every cell below n is
 // valid and is its own token index.  CandidateRow: cell c*P + i is token
 // cand[c]*P + i, and a cell holding -inf is not a candidate (the candidate scorer writes
@@ -538,6 +563,72 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int n, i
   }
 
   // ---- large bucket (long runs of equal values): the exact path ----
+  topk_row_exact<NT, EPT, Map>(row, n, k, out, &sh, map, d1, kk, ne);
+}
+
+// Top-k of a row too long to keep in registers (more than 32 cells per thread: at 1024
+// threads, 64 keys each spilled about 110 registers and a 65536-cell row took 43.7 us;
+// re-reading the cells per pass, 25.1 us).
+// The same passes in the same order as topk_row, so the same output bytes, but every pass
+// over the cells re-reads them (from the cache after the first) instead of holding keys.
+template <int NT, int EPT, class Map = DenseRow>
+__device__ __forceinline__ void topk_row_stream(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
+                                                TopkShared<NT, EPT>& sh, const Map map = Map()) {
+  using C = Cfg<NT>;
+  const int tid = threadIdx.x;
+  if (n <= (Map::kCountValid ? 0 : k)) {  // uniform
+    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? map.token(i) : -1;
+    return;
+  }
+  const int ne = __builtin_amdgcn_readfirstlane((n + NT - 1) / NT);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, n * 4, kBufferRsrcFlags);
+  auto load = [&](int e) {  // a cell past n reads 0, masked to key 0 below
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, e * NT * 4, 0));
+  };
+  auto key_of = [&](int e, float f) { return map.key(f, e * NT + tid - n); };
+  for (int i = tid; i < C::Bins / 4 + 64; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0, 0, 0, 0);
+  if constexpr (Map::kCountValid) {
+    int cnt = 0;
+    stream_rounds<EPT>(load, [&](int e, float f) { cnt += key_of(e, f) != 0u ? 1 : 0; });
+    int total;
+    int pos = block_excl_scan<NT>(cnt, sh.wave_tot, total);
+    if (total <= k) {  // uniform
+      stream_rounds<EPT>(load, [&](int e, float f) {
+        if (key_of(e, f) != 0u) out[pos++] = map.token(e * NT + tid);
+      });
+      for (int i = total + tid; i < k; i += NT) out[i] = -1;
+      return;
+    }
+  }
+  __syncthreads();
+  stream_rounds<EPT>(load, [&](int e, float f) {
+    const uint32_t kv = key_of(e, f);
+    if (kv != 0u) atomicAdd(&sh.hist[kv >> C::Shift], 1u);
+  });
+  __syncthreads();
+  select_digit<NT, C::Bins>(sh, k);
+  const uint32_t d1 = (uint32_t)sh.sel_digit;
+  int kk = k - sh.sel_above;
+  int n_gt = 0, n_in = 0;
+  stream_rounds<EPT>(load, [&](int e, float f) {
+    const uint32_t dg = key_of(e, f) >> C::Shift;
+    n_gt += dg > d1 ? 1 : 0;
+    n_in += dg == d1 ? 1 : 0;
+  });
+  int tot_gt, nc, pos_gt, pos_in;
+  block_excl_scan2<NT>(n_gt, n_in, sh.wave_tot, pos_gt, pos_in, tot_gt, nc);
+  if (nc <= kRankCap) {
+    stream_rounds<EPT>(load, [&](int e, float f) {
+      const uint32_t kv = key_of(e, f);
+      const uint32_t dg = kv >> C::Shift;
+      if (dg == d1) sh.cand[pos_in++] = ((uint64_t)kv << 32) | (uint32_t)~(e * NT + tid);
+      else if (dg > d1) out[pos_gt++] = map.token(e * NT + tid);
+    });
+    __syncthreads();
+    rank_bucket<NT>(sh, nc, kk, tot_gt, out, map);
+    return;
+  }
   topk_row_exact<NT, EPT, Map>(row, n, k, out, &sh, map, d1, kk, ne);
 }
 

@@ -41,6 +41,8 @@ def gpu_topk(logits_d, ctx, B, n_q, k):
     (2600, 2, (900, 5000), 300, False),      # many rows, n_q 2, small k
     (2048, 1, (16000, 16384), 1024, True),   # many long rows with ties
     (64, 1, (2000, 8192), 3000, False),      # a large k, some rows shorter than it
+    (4, 1, (40000, 65536), 1024, True),      # rows past 32 cells per thread (re-read passes), ties
+    (3, 1, (33000, 65536), 37, False),       # the same with a small k
 ])
 def test_topk_isolated_exact(rows, n_q, lens, k, ties):
     rng = np.random.default_rng(rows * 7 + k + int(ties))
