@@ -331,15 +331,17 @@ hipError_t launch_logits_stream(const LogitsArgs& a, int num_cus, hipStream_t s)
   if (a.max_ctx == 0) return hipSuccess;
   if (!logits_stream_takes(a.B, a.n_q, a.max_ctx)) return hipErrorInvalidValue;
   const int ht = (a.H + kHeadTile - 1) / kHeadTile;
-  // Two waves per SIMD of one-row workers, or six blocks per CU of several-row workers
-  // (fewer, longer runs measured faster than a fuller device: the page ids and query
-  // tiles are loaded once per run); at least two workers per sequence (so the balanced
-  // runs have room), and no more workers than chunks.  Runs are at most q_cap chunks, so
-  // that a run's pages fit the 64-entry page-id window: with spare >= max_units / q_cap
-  // workers past one per sequence, the device's q = ceil(U / spare) <= q_cap.
+  // Two waves per SIMD of one-row MXFP4 workers, four of FP8 ones (whose 132-byte rows
+  // take two loads each: large pool 77.4-78.1 -> 76.4 us, while MXFP4 measured slower with
+  // more), or six blocks per CU of several-row workers (fewer, longer runs measured faster
+  // than a fuller device: the page ids and query tiles are loaded once per run); at least
+  // two workers per sequence (so the balanced runs have room), and no more workers than
+  // chunks.  Runs are at most q_cap chunks, so that a run's pages fit the 64-entry page-id
+  // window: with spare >= max_units / q_cap workers past one per sequence, the device's
+  // q = ceil(U / spare) <= q_cap.
   const int64_t max_units = (int64_t)a.B * ((a.max_ctx + 63) / 64);
   const int64_t q_cap = std::max<int64_t>(1, (int64_t)63 * a.pool.page_size / 64);
-  int64_t workers = a.n_q == 1 ? (int64_t)num_cus * 8 : (int64_t)num_cus * 6;
+  int64_t workers = a.n_q == 1 ? (int64_t)num_cus * (a.pool.kv_format == 0 ? 8 : 16) : (int64_t)num_cus * 6;
   workers = std::max<int64_t>(workers, 2 * (int64_t)a.B);
   workers = std::max<int64_t>(workers, (max_units + q_cap - 1) / q_cap + a.B);
   workers = std::min<int64_t>(workers, max_units + a.B);
