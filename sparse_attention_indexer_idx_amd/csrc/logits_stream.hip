@@ -7,7 +7,8 @@
 // W workers, every worker takes a contiguous run of at most q = ceil(U / (W - B)) chunks of
 // one sequence (sequence b gets ceil(chunks_b / q) workers), so long and short sequences
 // finish together and a worker's query tiles stay the same throughout its run.  Each wave
-// computes U, q and its own run from the lengths (a wave-wide prefix over the sequences).
+// computes U, q and its own run from the lengths (a wave-wide prefix over the sequences);
+// the runs are laid out in order over the XCDs, so a sequence's runs mostly share one L2.
 // A worker is a wave when n_q = 1; for n_q = 2..4 it is a block whose four waves stage a
 // chunk's K tiles in LDS and whose wave j scores query row j from them, so a chunk's K
 // leaves HBM once per block.  A run's page ids are loaded once (RunPages), and the launch
