@@ -3,7 +3,8 @@
 //
 // One workgroup per row.  The row's valid cells are held in registers as order-
 // preserving 32-bit keys (thread t holds cells t, t+NT, t+2NT, ...: every load is a
-// contiguous 256-byte wave access, and all of a row's loads are in flight together).
+// contiguous 256-byte wave access, and all of a row's loads are in flight together); a row
+// of more than 32 cells per thread is re-read for each pass instead (topk_row_stream).
 //   pass 1 — an LDS histogram of the top D1 key bits (13 for 1024-thread rows, 12 for
 //            smaller blocks, which share a CU several at a time) picks the digit d1
 //            holding the k-th key: cells above d1 are selected, cells below are not;
